@@ -1,0 +1,217 @@
+"""Seeded synthetic inputs for the KDA operator (shared by tests, smoke and bench).
+
+This module only draws random numbers and rounds them to their storage type.
+It holds none of the operator's arithmetic, so both the fp64 oracle and the
+HIP path can consume its output without sharing any method code.
+
+Distributions (one reading of the workloads described for the operator):
+  q, k   ~ N(0, 1), then divided by their L2 norm over the head dimension
+           (computed in fp64 before rounding to the storage type);
+  v      ~ N(0, 1);
+  beta   = sigmoid(N(0, 1))                      (fp32, one scalar per token and head);
+  g      = log(alpha) = -softplus(N(0, 1) + 2)   (fp32, one value per key channel);
+  S_0    ~ N(0, std) with std 0.02 where the workload has an initial state.
+The second argument of N(., .) is a standard deviation.  A "weak decay"
+variant uses -softplus(N(0,1) - 5) (alpha close to 1) to stress long-range
+state propagation.
+
+Draw order for one generator: q, k, v, x_beta, x_alpha, S_0.
+Rounding to bf16 is round-to-nearest-even on the fp32 value.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+SEED_BASE = 93000
+CHUNK = 64
+
+
+# --------------------------------------------------------------------------- bf16 storage
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 array -> uint16 bf16 bit patterns, round-to-nearest-even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to the nearest bf16 value, kept in fp32 storage."""
+    return bf16_to_f32(bf16_bits(x))
+
+
+def _store(x: np.ndarray, io: str) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float32)
+    return bf16_round(x) if io == "bf16" else x
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    x = x.astype(np.float64)
+    return np.where(x > 30.0, x, np.log1p(np.exp(np.minimum(x, 30.0))))
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
+
+
+def _unit_rows(x: np.ndarray, block: int = 1 << 20) -> np.ndarray:
+    """Divide each last-axis row by its L2 norm (fp64 norm), returned as fp32."""
+    flat = x.reshape(-1, x.shape[-1])
+    out = np.empty(flat.shape, dtype=np.float32)
+    for s in range(0, flat.shape[0], block):
+        blk = flat[s:s + block].astype(np.float64)
+        nrm = np.sqrt(np.sum(blk * blk, axis=-1, keepdims=True))
+        out[s:s + block] = (blk / np.maximum(nrm, 1e-300)).astype(np.float32)
+    return out.reshape(x.shape)
+
+
+# --------------------------------------------------------------------------- containers
+@dataclasses.dataclass
+class KDAInputs:
+    """One batch of operator inputs, all in fp32 storage (bf16-valued when io == 'bf16').
+
+    Layout: q, k, g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
+    S0 [N, H, dk, dv] or None; cu_seqlens [N + 1] int32 or None (then B == 1).
+    """
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    g: np.ndarray
+    beta: np.ndarray
+    S0: Optional[np.ndarray]
+    cu_seqlens: Optional[np.ndarray]
+    io: str
+    scale: float = 1.0
+
+    @property
+    def B(self): return self.q.shape[0]
+    @property
+    def T(self): return self.q.shape[1]
+    @property
+    def H(self): return self.q.shape[2]
+    @property
+    def dk(self): return self.q.shape[3]
+    @property
+    def dv(self): return self.v.shape[3]
+    @property
+    def N(self):
+        return self.B if self.cu_seqlens is None else len(self.cu_seqlens) - 1
+
+    def seq_bounds(self, n: int):
+        """(batch index, first token, length) of sequence n."""
+        if self.cu_seqlens is None:
+            return n, 0, self.T
+        s, e = int(self.cu_seqlens[n]), int(self.cu_seqlens[n + 1])
+        return 0, s, e - s
+
+
+def draw_tokens(rng: np.random.Generator, shape_tok, H: int, dk: int, dv: int, io: str,
+                g_shift: float = 2.0, normalize_qk: bool = True):
+    """Draw q, k, v, beta, g for tokens of shape `shape_tok` (e.g. (B, T)), in the fixed order."""
+    q = rng.standard_normal((*shape_tok, H, dk), dtype=np.float32)
+    k = rng.standard_normal((*shape_tok, H, dk), dtype=np.float32)
+    v = rng.standard_normal((*shape_tok, H, dv), dtype=np.float32)
+    xb = rng.standard_normal((*shape_tok, H), dtype=np.float32)
+    xa = rng.standard_normal((*shape_tok, H, dk), dtype=np.float32)
+    if normalize_qk:
+        q = _unit_rows(q)
+        k = _unit_rows(k)
+    beta = _sigmoid(xb).astype(np.float32)
+    g = (-_softplus(xa.astype(np.float64) + g_shift)).astype(np.float32)
+    return _store(q, io), _store(k, io), _store(v, io), beta, g
+
+
+def make_dense(B: int, T: int, H: int, dk: int, dv: int, io: str, seed: int,
+               s0_std: Optional[float] = None, g_shift: float = 2.0) -> KDAInputs:
+    rng = np.random.default_rng(seed)
+    q, k, v, beta, g = draw_tokens(rng, (B, T), H, dk, dv, io, g_shift)
+    S0 = None
+    if s0_std is not None:
+        S0 = (rng.standard_normal((B, H, dk, dv), dtype=np.float32) * np.float32(s0_std))
+    return KDAInputs(q, k, v, g, beta, S0, None, io)
+
+
+def varlen_lengths(n_seq: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi, size=n_seq, endpoint=True).astype(np.int64)
+
+
+def make_varlen(lengths, H: int, dk: int, dv: int, io: str, seed: int,
+                s0_std: Optional[float] = 0.02, g_shift: float = 2.0,
+                normalize_qk: bool = True) -> KDAInputs:
+    """Packed batch: sequence n is drawn from default_rng([seed, n]) (q, k, v, beta, g, S0)."""
+    lengths = [int(x) for x in lengths]
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    Ttot = int(cu[-1])
+    q = np.empty((1, Ttot, H, dk), np.float32)
+    k = np.empty((1, Ttot, H, dk), np.float32)
+    v = np.empty((1, Ttot, H, dv), np.float32)
+    g = np.empty((1, Ttot, H, dk), np.float32)
+    beta = np.empty((1, Ttot, H), np.float32)
+    S0 = np.empty((len(lengths), H, dk, dv), np.float32) if s0_std is not None else None
+    for n, L in enumerate(lengths):
+        rng = np.random.default_rng([seed, n])
+        qn, kn, vn, bn, gn = draw_tokens(rng, (L,), H, dk, dv, io, g_shift, normalize_qk)
+        s, e = cu[n], cu[n + 1]
+        q[0, s:e], k[0, s:e], v[0, s:e], beta[0, s:e], g[0, s:e] = qn, kn, vn, bn, gn
+        if S0 is not None:
+            S0[n] = rng.standard_normal((H, dk, dv), dtype=np.float32) * np.float32(s0_std)
+    return KDAInputs(q, k, v, g, beta, S0, cu.astype(np.int32), io)
+
+
+def decode_step_inputs(N: int, H: int, d: int, io: str, seed: int, step: int,
+                       g_shift: float = 2.0):
+    """Token inputs of one decode step: q, k, v [N, H, d], g [N, H, d], beta [N, H]."""
+    rng = np.random.default_rng([seed, step])
+    q, k, v, beta, g = draw_tokens(rng, (N,), H, d, d, io, g_shift)
+    return q, k, v, g, beta
+
+
+def decode_initial_state(N: int, H: int, d: int, seed: int, std: float = 0.02) -> np.ndarray:
+    rng = np.random.default_rng([seed, 1 << 20])
+    return rng.standard_normal((N, H, d, d), dtype=np.float32) * np.float32(std)
+
+
+def prep_inputs(lengths, H: int, d: int, io: str, seed: int, w_std: float = 0.5, width: int = 4):
+    """Raw (un-normalised) x [1, Ntok, H, d] ~ N(0,1), conv weights [H*d, width] ~ N(0, w_std)."""
+    lengths = [int(x) for x in lengths]
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((H * d, width), dtype=np.float32) * np.float32(w_std))
+    x = np.empty((1, int(cu[-1]), H, d), np.float32)
+    for n, L in enumerate(lengths):
+        r = np.random.default_rng([seed, n])
+        x[0, cu[n]:cu[n + 1]] = _store(r.standard_normal((L, H, d), dtype=np.float32), io)
+    return x, w, cu.astype(np.int32)
+
+
+# --------------------------------------------------------------------------- named workloads
+def config0() -> KDAInputs:
+    """fp32 recurrence: B=1, H=2, T=256, d=64, S0 = 0."""
+    return make_dense(1, 256, 2, 64, 64, "f32", SEED_BASE + 0)
+
+
+def config1() -> KDAInputs:
+    """Chunked prefill: B=4, H=16, T=4096, d=128, bf16 q/k/v, S0 = 0."""
+    return make_dense(4, 4096, 16, 128, 128, "bf16", SEED_BASE + 1)
+
+
+def config2() -> KDAInputs:
+    """Long-context prefill: B=1, H=32, T=131072, d=128, bf16 q/k/v, S0 ~ N(0, 0.02)."""
+    return make_dense(1, 131072, 32, 128, 128, "bf16", SEED_BASE + 2, s0_std=0.02)
+
+
+CONFIG3 = dict(N=256, H=32, d=128, steps=100, seed=SEED_BASE + 3)
+CONFIG4 = dict(n_seq=64, lo=512, hi=16384, H=32, d=128, seed=SEED_BASE + 4)
+
+
+def config4_lengths() -> np.ndarray:
+    return varlen_lengths(CONFIG4["n_seq"], CONFIG4["lo"], CONFIG4["hi"], CONFIG4["seed"])
