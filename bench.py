@@ -1,0 +1,249 @@
+"""Benchmark of the KDA operator on one MI355X.
+
+One step = one chunked prefill (kda_fwd) of the 4 x 4096-token, 16-head, d = 128 batch
+(bf16 q/k/v, fp32 log-decay/beta/state, chunk 64): the headline "prefill tokens/s".
+The same run also measures
+  * the decode step (256 sequences x 32 heads, d = 128, fp32 state resident in HBM,
+    100 consecutive steps): state GB/s and fraction of HBM peak;
+  * the q/k prologue on the packed 64-sequence batch (lengths U[512, 16384], H = 32):
+    GB/s;
+  * the fp64 CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
+Per-kernel times come from HIP events recorded on the stream the kernels run on.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-prep]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+METRIC = "KDA prefill tokens/s + MFMA %; decode-step state GB/s + % HBM peak"
+
+# Algorithmic work per token-head of the prefill (d = 128, chunk 64): the inputs q, k, v (bf16)
+# and g (fp32), beta, the output o (bf16): 3*256 + 512 + 4 + 256 bytes; flops of the chunkwise
+# form (triangle-aware): 140.5 KFLOP.
+PREFILL_IN_BYTES = 3 * 256 + 512 + 4
+PREFILL_OUT_BYTES = 256
+PREFILL_FLOP = 140.5e3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def bf16_dev(x, dev):
+    import torch
+    import kda_inputs as ki
+    return torch.from_numpy(ki.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_events(fn, reps, torch):
+    """Average ms of fn() over reps, with HIP events on the current stream."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def bench_prefill(args, torch, kda, dev):
+    import kda_inputs as ki
+    inp = ki.config1()
+    B, T, H, d = inp.B, inp.T, inp.H, inp.dk
+    q, k, v = (bf16_dev(x, dev) for x in (inp.q, inp.k, inp.v))
+    g = torch.from_numpy(inp.g).to(dev)
+    beta = torch.from_numpy(inp.beta).to(dev)
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = kda.fwd_workspace_bytes(kda.KDA_BF16, B, T, H, d, d, B, False)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    L = kda.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+
+    def step():
+        rc = L.kda_fwd(kda.KDA_BF16, B, T, H, d, d, None, B, p(q), p(k), p(v), p(g), p(beta), 1.0, None, p(S),
+                       p(o), p(ws), nws, stream)
+        assert rc == 0, kda.status_string(rc)
+
+    def local():
+        assert L.kda_fwd_chunk_local(kda.KDA_BF16, B, T, H, d, d, None, B, p(q), p(k), p(v), p(g), p(beta),
+                                     p(ws), nws, stream) == 0
+
+    def scan():
+        assert L.kda_fwd_state_scan(kda.KDA_BF16, B, T, H, d, d, None, B, 1.0, None, p(S), p(o), p(ws), nws,
+                                    stream) == 0
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    # per-kernel times (events around each phase launch, same stream)
+    reps = max(args.steps, 5)
+    ms_local = time_events(local, reps, torch)
+    ms_scan = time_events(scan, reps, torch)
+    ms_fwd = time_events(step, reps, torch)
+    tokens = B * T
+    token_heads = B * T * H
+    res = dict(tokens=tokens, token_heads=token_heads, ms_step=ms_step, ms_fwd_events=ms_fwd,
+               ms_chunk_local=ms_local, ms_state_scan=ms_scan,
+               ws_bytes_per_chunk_head=nws // (B * ((T + 63) // 64) * H))
+    return res, inp
+
+
+def bench_decode(args, torch, kda, dev):
+    N, H, d, steps = 256, 32, 128, 100
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93003)
+    state = (torch.randn((N, H, d, d), generator=gen, device=dev, dtype=torch.float32) * 0.02).contiguous()
+
+    def unit(x):
+        return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16).contiguous()
+
+    toks = []
+    for _ in range(steps):
+        q = unit(torch.randn((N, H, d), generator=gen, device=dev))
+        k = unit(torch.randn((N, H, d), generator=gen, device=dev))
+        v = torch.randn((N, H, d), generator=gen, device=dev).to(torch.bfloat16)
+        beta = torch.sigmoid(torch.randn((N, H), generator=gen, device=dev)).contiguous()
+        g = (-torch.nn.functional.softplus(torch.randn((N, H, d), generator=gen, device=dev) + 2)).contiguous()
+        toks.append((q, k, v, g, beta))
+    o = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    L = kda.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+
+    def run(s):
+        q, k, v, g, beta = toks[s % steps]
+        assert L.kda_decode_step(kda.KDA_BF16, N, H, d, d, p(q), p(k), p(v), p(g), p(beta), 1.0, p(state),
+                                 p(o), stream) == 0
+
+    for s in range(5):
+        run(s)
+    torch.cuda.synchronize()
+    it = iter(range(steps))
+    ms = time_events(lambda: run(next(it)), steps, torch)
+    state_bytes = 2 * N * H * d * d * 4
+    io_bytes = N * H * (3 * d * 2 + d * 4 + 4 + d * 2)
+    return dict(ms_step=ms, state_bytes=state_bytes, io_bytes=io_bytes,
+                state_gbs=state_bytes / ms / 1e6, total_gbs=(state_bytes + io_bytes) / ms / 1e6)
+
+
+def bench_prep(args, torch, kda, dev):
+    import kda_inputs as ki
+    lengths = ki.config4_lengths()
+    H, d = 32, 128
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    ntok = int(cu[-1])
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93004)
+    x = torch.randn((1, ntok, H, d), generator=gen, device=dev).to(torch.bfloat16)
+    w = (torch.randn((H * d, 4), generator=gen, device=dev) * 0.5).contiguous()
+    y = torch.empty_like(x)
+    cu_d = torch.from_numpy(cu).to(dev)
+    for _ in range(2):
+        kda.prep(x, w, cu_d, y=y)
+    ms = time_events(lambda: kda.prep(x, w, cu_d, y=y), 5, torch)
+    nbytes = 2 * ntok * H * d * 2
+    return dict(ms=ms, tokens=ntok, bytes=nbytes, gbs=nbytes / ms / 1e6)
+
+
+def cpu_baseline(inp):
+    import oracle
+    threads = oracle.default_threads()
+    R = oracle.Recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+    t0 = time.perf_counter()
+    R.run(threads=threads)
+    wall = time.perf_counter() - t0
+    tokens = inp.B * inp.T
+    return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole prefill batch: all {inp.B * inp.H} (sequence, head) chains of "
+                      f"{inp.T} tokens, fp64 token recurrence, {wall:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator shards by head and sequence with no exchange)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gated_delta_rule_93_amd as kda
+    dev = torch.device("cuda:0")
+    kda.lib()
+
+    log("prefill ...")
+    pf, inp = bench_prefill(args, torch, kda, dev)
+    token_heads = pf["token_heads"]
+    value = pf["tokens"] / (pf["ms_step"] / 1e3)
+    # dominant prefill kernel and its roofline (HBM-bound by arithmetic intensity)
+    if pf["ms_chunk_local"] >= pf["ms_state_scan"]:
+        dom, dom_ms, dom_bytes = "chunk_local_kernel", pf["ms_chunk_local"], PREFILL_IN_BYTES * token_heads
+    else:
+        dom, dom_ms, dom_bytes = "chunk_scan_kernel", pf["ms_state_scan"], PREFILL_OUT_BYTES * token_heads
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+    flops = PREFILL_FLOP * token_heads
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": pf["ms_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "KDA chunked prefill B=4 H=16 T=4096 d_k=d_v=128 chunk=64, bf16 q/k/v, "
+                               "fp32 log-decay/beta/state", "global_batch": 4, "seq_len": 4096, "heads": 16,
+                   "head_dim": 128, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_bytes, "ms_per_launch": dom_ms},
+        "prefill": {"ms_fwd": pf["ms_fwd_events"], "ms_chunk_local": pf["ms_chunk_local"],
+                    "ms_state_scan": pf["ms_state_scan"],
+                    "algorithmic_GBs": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * token_heads / pf["ms_fwd_events"] / 1e6,
+                    "algorithmic_TFLOPs": flops / pf["ms_fwd_events"] / 1e9,
+                    "mfma_frac_of_bf16_peak": flops / pf["ms_fwd_events"] / 1e9 / BF16_PEAK_TFLOPS,
+                    "workspace_bytes_per_chunk_head": pf["ws_bytes_per_chunk_head"]},
+    }
+    if not args.no_decode:
+        log("decode ...")
+        dc = bench_decode(args, torch, kda, dev)
+        out["decode"] = {"workload": "256 sequences x 32 heads, d=128, fp32 state, bf16 tokens, 100 steps",
+                         "ms_per_step": dc["ms_step"], "state_GBs": dc["state_gbs"], "total_GBs": dc["total_gbs"],
+                         "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": dc["total_gbs"],
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": dc["total_gbs"] / HBM_PEAK_GBS, "traffic": None}}
+    if not args.no_prep:
+        log("prep ...")
+        pr = bench_prep(args, torch, kda, dev)
+        out["prep"] = {"workload": f"{pr['tokens']} packed tokens (64 sequences), H=32, d=128, width 4, bf16",
+                       "ms": pr["ms"], "GBs": pr["gbs"], "frac": pr["gbs"] / HBM_PEAK_GBS}
+    if not args.no_cpu:
+        log("cpu baseline ...")
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""Python binding of libkda.so, the MI355X Kimi Delta Attention operator (C ABI in include/kda.h).
+
+Argument marshalling only: every step of the operator runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU fallback: if the
+library is missing, importing works but the first call raises.
+
+    o, S = fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None)
+    o    = decode_step(q, k, v, g, beta, state, scale=1.0)     # state updated in place
+    y    = prep(x, conv_w, cu_seqlens=None)
+
+Layouts: q, k, g [B, T, H, dk]; v, o [B, T, H, dv]; beta [B, T, H]; states [N, H, dk, dv]
+fp32 with element (i, j) mapping key channel i to value channel j (o = S^T q).  q, k, v
+(and x) are bfloat16 or float32; g = log(alpha), beta and states are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_LAUNCH = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(msg)
+        self.code = code
+
+
+def lib():
+    """The loaded libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                               "g.build()'` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.kda_status_string.argtypes = [I]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+        L.kda_fwd_workspace_bytes.restype = S
+        L.kda_fwd.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, F, P, P, P, P, S, P]
+        L.kda_fwd.restype = I
+        L.kda_fwd_chunk_local.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, P, S, P]
+        L.kda_fwd_chunk_local.restype = I
+        L.kda_fwd_state_scan.argtypes = [I, I, I, I, I, I, P, I, F, P, P, P, P, S, P]
+        L.kda_fwd_state_scan.restype = I
+        L.kda_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, F, P, P, P]
+        L.kda_decode_step.restype = I
+        L.kda_prep.argtypes = [I, I, I, I, I, P, I, P, P, I, P, P]
+        L.kda_prep.restype = I
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().kda_status_string(int(code)).decode()
+
+
+def _check(code: int):
+    if code != KDA_OK:
+        raise KDAError(code, status_string(code))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_dtype(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def fwd_workspace_bytes(io: int, B: int, T: int, H: int, dk: int, dv: int, N: int, varlen: bool) -> int:
+    return int(lib().kda_fwd_workspace_bytes(io, B, T, H, dk, dv, N, 1 if varlen else 0))
+
+
+def fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=None,
+        output_final_state: bool = True, o=None, final_state=None, workspace=None,
+        stream=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Chunked prefill (kda_fwd).  Returns (o, final_state or None)."""
+    torch = _torch()
+    io = _io_dtype(q)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, dk))
+    _need(v, "v", q.dtype, (B, T, H, dv))
+    _need(g, "g", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(o, "o", q.dtype, (B, T, H, dv))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    elif final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, dk, dv))
+    need = fwd_workspace_bytes(io, B, T, H, dk, dv, N, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().kda_fwd(io, B, T, H, dk, dv, _ptr(cu_seqlens), N,
+                         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                         _ptr(initial_state), _ptr(final_state), _ptr(o),
+                         _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o, final_state
+
+
+def decode_step(q, k, v, g, beta, state, scale: float = 1.0, o=None, stream=None):
+    """One token for N sequences (kda_decode_step); `state` [N, H, dk, dv] is updated in place."""
+    torch = _torch()
+    io = _io_dtype(q)
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (N, H, dk))
+    _need(v, "v", q.dtype, (N, H, dv))
+    _need(g, "g", torch.float32, (N, H, dk))
+    _need(beta, "beta", torch.float32, (N, H))
+    _need(state, "state", torch.float32, (N, H, dk, dv))
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=q.dtype, device=q.device)
+    else:
+        _need(o, "o", q.dtype, (N, H, dv))
+    _check(lib().kda_decode_step(io, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 float(scale), _ptr(state), _ptr(o), _stream(stream)))
+    return o
+
+
+def prep(x, conv_w, cu_seqlens=None, y=None, stream=None):
+    """q/k prologue (kda_prep): causal depthwise conv (width conv_w.shape[1]) -> SiLU -> L2 norm."""
+    torch = _torch()
+    io = _io_dtype(x)
+    B, T, H, d = x.shape
+    W = conv_w.shape[1]
+    _need(x, "x", x.dtype)
+    _need(conv_w, "conv_w", torch.float32, (H * d, W))
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+    if y is None:
+        y = torch.empty_like(x)
+    else:
+        _need(y, "y", x.dtype, tuple(x.shape))
+    _check(lib().kda_prep(io, B, T, H, d, _ptr(cu_seqlens), N, _ptr(x), _ptr(conv_w), W, _ptr(y),
+                          _stream(stream)))
+    return y

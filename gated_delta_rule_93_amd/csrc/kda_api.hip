@@ -1,0 +1,158 @@
+// kda_api.hip -- extern "C" entry points of libkda.so: argument validation and launches.
+// Semantics, layouts and error behaviour are documented in include/kda.h.
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_d(int d) { return d == 64 || d == 128; }
+bool valid_dtype(kda_dtype_t io) { return io == KDA_F32 || io == KDA_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK: success";
+        case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT: null pointer, bad size, misaligned buffer or bad dtype";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid arguments that this build does not implement";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
+        case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    }
+    return "KDA: unknown status";
+}
+
+size_t kda_fwd_workspace_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, int N, int varlen) {
+    if (!valid_dtype(io) || B < 0 || T < 0 || H < 0 || N < 0) return 0;
+    if (d_k != d_v || !supported_d(d_k)) return 0;
+    if (varlen && B != 1) return 0;
+    const long slots = kda::fwd_chunk_slots(B, T, N, varlen != 0);
+    return (size_t)slots * (size_t)H * kda::fwd_bytes_per_chunk_head(io == KDA_BF16, d_k);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by kda_fwd and its two phases.  Pointers passed as `nullptr_ok` sentinels
+// are not required by the calling phase.
+enum FwdPart { kLocal = 1, kScan = 2, kBoth = 3 };
+
+kda_status_t check_fwd(int part, kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                       const int32_t *cu_seqlens, int N, const void *q, const void *k, const void *v,
+                       const float *g, const float *beta, const float *s0, const float *sN, const void *o,
+                       const void *workspace, size_t workspace_bytes) {
+    if (!valid_dtype(io) || B < 0 || T < 0 || H < 0 || N < 0 || d_k <= 0 || d_v <= 0)
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (cu_seqlens) {
+        if (B != 1) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+    } else if (N != B) {
+        return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (d_k != d_v || !supported_d(d_k)) return KDA_ERR_UNSUPPORTED;
+    const long tokens = (long)B * T;
+    if (tokens > 0 && H > 0) {
+        if (part & kLocal) {
+            if (!q || !k || !v || !g || !beta) return KDA_ERR_INVALID_ARGUMENT;
+            if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g)) return KDA_ERR_INVALID_ARGUMENT;
+        }
+        if (part & kScan) {
+            if (!o || !aligned16(o)) return KDA_ERR_INVALID_ARGUMENT;
+        }
+    }
+    if ((part & kScan) && ((s0 && !aligned16(s0)) || (sN && !aligned16(sN)))) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t need = kda_fwd_workspace_bytes(io, B, T, H, d_k, d_v, N, cu_seqlens != nullptr);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KDA_ERR_WORKSPACE;
+    return KDA_OK;
+}
+
+kda::FwdArgs fwd_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens, int N,
+                      const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
+                      const float *s0, float *sN, void *o, void *workspace) {
+    kda::FwdArgs a;
+    a.bf16 = io == KDA_BF16;
+    a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.N = N;
+    a.cu_seqlens = cu_seqlens;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.scale = scale;
+    a.s0 = s0; a.sN = sN; a.o = o; a.ws = workspace;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_fwd(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens, int N,
+                     const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
+                     const float *initial_state, float *final_state, void *o, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    kda_status_t st = check_fwd(kBoth, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, initial_state,
+                                final_state, o, workspace, workspace_bytes);
+    if (st != KDA_OK || (long)N * H == 0) return st;
+    const kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, scale, initial_state,
+                                    final_state, o, workspace);
+    return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_fwd_chunk_local(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,
+                                 int N, const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    kda_status_t st = check_fwd(kLocal, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, nullptr, nullptr,
+                                nullptr, workspace, workspace_bytes);
+    if (st != KDA_OK || (long)N * H == 0) return st;
+    const kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, 1.f, nullptr, nullptr,
+                                    nullptr, workspace);
+    return kda::launch_fwd_local(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_fwd_state_scan(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,
+                                int N, float scale, const float *initial_state, float *final_state, void *o,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    kda_status_t st = check_fwd(kScan, io, B, T, H, d_k, d_v, cu_seqlens, N, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, initial_state, final_state, o, workspace, workspace_bytes);
+    if (st != KDA_OK || (long)N * H == 0) return st;
+    const kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, scale, initial_state, final_state, o, workspace);
+    return kda::launch_fwd_scan(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_decode_step(kda_dtype_t io, int N, int H, int d_k, int d_v, const void *q, const void *k,
+                             const void *v, const float *g, const float *beta, float scale, float *state, void *o,
+                             hipStream_t stream) {
+    if (!valid_dtype(io) || N < 0 || H < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!supported_d(d_k) || !supported_d(d_v)) return KDA_ERR_UNSUPPORTED;
+    if ((long)N * H == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(state) || !aligned16(o))
+        return KDA_ERR_INVALID_ARGUMENT;
+    kda::DecodeArgs a;
+    a.bf16 = io == KDA_BF16;
+    a.N = N; a.H = H; a.dk = d_k; a.dv = d_v;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.scale = scale; a.state = state; a.o = o;
+    return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_prep(kda_dtype_t io, int B, int T, int H, int d, const int32_t *cu_seqlens, int N, const void *x,
+                      const float *conv_w, int W, void *y, hipStream_t stream) {
+    if (!valid_dtype(io) || B < 0 || T < 0 || H < 0 || d <= 0 || N < 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (W < 1 || W > 8) return W < 1 ? KDA_ERR_INVALID_ARGUMENT : KDA_ERR_UNSUPPORTED;
+    if (cu_seqlens) {
+        if (B != 1 || N < 1) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    if (!supported_d(d)) return KDA_ERR_UNSUPPORTED;
+    if ((long)B * T * H == 0) return KDA_OK;
+    if (!x || !conv_w || !y) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(conv_w)) return KDA_ERR_INVALID_ARGUMENT;
+    if (x == y) return KDA_ERR_INVALID_ARGUMENT;
+    kda::PrepArgs a;
+    a.bf16 = io == KDA_BF16;
+    a.B = B; a.T = T; a.H = H; a.d = d; a.W = W; a.N = cu_seqlens ? N : B;
+    a.cu_seqlens = cu_seqlens; a.x = x; a.w = conv_w; a.y = y;
+    return kda::launch_prep(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"

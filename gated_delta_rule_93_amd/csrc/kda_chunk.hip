@@ -1,0 +1,618 @@
+// kda_chunk.hip -- chunked KDA prefill: a chunk-local kernel and a serial state-scan kernel.
+//
+// The pages state that deployment uses a chunkwise parallel form, the WY representation with
+// a UT transform (page "Kimi K3 注意力三件套", KDA section), i.e. parallel work inside a chunk
+// and a serial pass across chunks (blog post-114, chapter 3).  They leave out the algebra; the
+// form used here follows from unrolling the course page's section-3 update over one chunk of
+// C <= 64 tokens with incoming state S (per channel G_t = sum_{s<=t} g_s, gamma = G_last):
+//
+//   Akk[t,j] = beta_t sum_c k_tc k_jc e^{G_tc - G_jc}   (j < t)      Tm = (I + Akk)^-1
+//   Aqk[t,j] =        sum_c q_tc k_jc e^{G_tc - G_jc}   (j <= t)     T' = Tm Diag(beta)
+//   W = T' (K * e^G),  U = T' V,  Qh = Q * e^G,  Kh = K * e^{gamma - G}
+//   Ud = U - W S;   O = scale (Qh S + Aqk Ud);   S <- Diag(e^gamma) S + Kh^T Ud
+//
+// Kernel 1 (chunk_local_kernel): one 256-thread workgroup per (chunk, head), fully parallel.
+//   It builds the cumulative log-decay in LDS, the two decayed Gram matrices, the UT
+//   transform Tm by blocked forward substitution, and writes W, U, Qh, Kh^T, Aqk and
+//   e^gamma to the workspace, laid out as ready-to-load MFMA operand fragments.
+// Kernel 2 (chunk_scan_kernel): one wave per (sequence, head, 16 value columns); it keeps its
+//   d_k x 16 slice of the fp32 state in MFMA accumulator registers and walks the chunks.
+//
+// Exponent safety.  Every e^{x} is evaluated with x <= 0 or with |x| bounded by a checked
+// half-span: the Gram matrices use 16-token sub-blocks with the sub-block's middle row m as
+// reference (row factor e^{G_i - G_m}, column factor e^{G_m - G_j}, and for blocks I > J the
+// per-channel bridge e^{G_mI - G_mJ} <= 1).  If some |G_i - G_m| exceeds 115 (log2 units) the
+// chunk takes an exact element-wise fallback instead.
+//
+// Precision (bf16 inputs).  The Gram operands, Tm, Aqk, S and Ud enter the MFMAs as hi + lo
+// bf16 pairs (about 16 significant bits); U stays fp32.  q, k, v are used as stored (exact).
+// The fp32 path uses fp32 MFMAs throughout.
+#include <type_traits>
+
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+// ------------------------------------------------------------------ operand precision
+template <bool BF16> struct Prec;
+template <> struct Prec<true> {
+    using Plain = FragB;
+    using Split = Frag2;
+    static constexpr int kPlainPlanes = 1;
+    static constexpr int kSplitPlanes = 2;
+    static __device__ __forceinline__ Plain plain(const float *x) { return make_fragB(x); }
+    static __device__ __forceinline__ Split split(const float *x) { return make_frag2(x); }
+    static __device__ __forceinline__ void st_plain(char *base, int, int f, int lane, const Plain &p) {
+        reinterpret_cast<bf16x8 *>(base)[f * 64 + lane] = p.h;
+    }
+    static __device__ __forceinline__ Plain ld_plain(const char *base, int, int f, int lane) {
+        return FragB{reinterpret_cast<const bf16x8 *>(base)[f * 64 + lane]};
+    }
+    static __device__ __forceinline__ void st_split(char *base, int nf, int f, int lane, const Split &p) {
+        reinterpret_cast<bf16x8 *>(base)[f * 64 + lane] = p.h;
+        reinterpret_cast<bf16x8 *>(base + (size_t)nf * 1024)[f * 64 + lane] = p.l;
+    }
+    static __device__ __forceinline__ Split ld_split(const char *base, int nf, int f, int lane) {
+        Frag2 r;
+        r.h = reinterpret_cast<const bf16x8 *>(base)[f * 64 + lane];
+        r.l = reinterpret_cast<const bf16x8 *>(base + (size_t)nf * 1024)[f * 64 + lane];
+        return r;
+    }
+};
+template <> struct Prec<false> {
+    using Plain = FragF;
+    using Split = FragF;
+    static constexpr int kPlainPlanes = 2;
+    static constexpr int kSplitPlanes = 2;
+    static __device__ __forceinline__ Plain plain(const float *x) { return make_fragF(x); }
+    static __device__ __forceinline__ Split split(const float *x) { return make_fragF(x); }
+    static __device__ __forceinline__ void st_plain(char *base, int nf, int f, int lane, const FragF &p) {
+        reinterpret_cast<f32x4 *>(base)[f * 64 + lane] = f32x4{p.v[0], p.v[1], p.v[2], p.v[3]};
+        reinterpret_cast<f32x4 *>(base + (size_t)nf * 1024)[f * 64 + lane] = f32x4{p.v[4], p.v[5], p.v[6], p.v[7]};
+    }
+    static __device__ __forceinline__ FragF ld_plain(const char *base, int nf, int f, int lane) {
+        const f32x4 a = reinterpret_cast<const f32x4 *>(base)[f * 64 + lane];
+        const f32x4 b = reinterpret_cast<const f32x4 *>(base + (size_t)nf * 1024)[f * 64 + lane];
+        return FragF{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
+    }
+    static __device__ __forceinline__ void st_split(char *base, int nf, int f, int lane, const FragF &p) {
+        st_plain(base, nf, f, lane, p);
+    }
+    static __device__ __forceinline__ FragF ld_split(const char *base, int nf, int f, int lane) {
+        return ld_plain(base, nf, f, lane);
+    }
+};
+
+// ------------------------------------------------------------------ workspace layout
+// Per (chunk slot, head): W, Qh fragments [tt][kb]; Kh^T fragments [rt][kb2]; Aqk fragments
+// (6 lower ones); U as accumulator tiles [jt][tt][lane] f32x4; e^gamma [D].
+template <bool BF16, int D> struct WsLayout {
+    static constexpr int NT = 4;           // 16-token tiles per chunk
+    static constexpr int NKB = D / 32;     // 32-channel k-blocks
+    static constexpr int NRT = D / 16;     // 16-channel tiles
+    static constexpr int nW = NT * NKB, nQ = NT * NKB, nK = NRT * 2, nA = 6;
+    static constexpr int PP = Prec<BF16>::kPlainPlanes, SP = Prec<BF16>::kSplitPlanes;
+    static constexpr size_t offW = 0;
+    static constexpr size_t offQ = offW + (size_t)nW * PP * 1024;
+    static constexpr size_t offK = offQ + (size_t)nQ * PP * 1024;
+    static constexpr size_t offA = offK + (size_t)nK * PP * 1024;
+    static constexpr size_t offU = offA + (size_t)nA * SP * 1024;
+    static constexpr size_t offE = offU + (size_t)NRT * NT * 1024;
+    static constexpr size_t bytes = (offE + (size_t)D * 4 + 255) / 256 * 256;
+};
+
+// lower Aqk fragment index of (token tile tt, token k-block kb2), kb2 <= tt / 2
+__device__ __forceinline__ int aidx(int tt, int kb2) { return tt < 2 ? tt : 2 + 2 * (tt - 2) + kb2; }
+
+__device__ __forceinline__ int mid_row(int I) { return 16 * I + 8; }
+
+// pair p -> (I, J), I >= J, in the order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) ...
+__device__ __forceinline__ void pair_ij(int p, int &I, int &J) {
+    I = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3;
+    J = p - I * (I + 1) / 2;
+}
+// off-diagonal pair (I > J) -> bridge index in (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+__device__ __forceinline__ int bridge_idx(int I, int J) { return (I - 1) * I / 2 + J; }
+
+// ------------------------------------------------------------------ chunk addressing
+struct ChunkPos {
+    bool valid;
+    int n, c, Cc;
+    long tok0;
+};
+// Largest n in [0, N) with n + cu[n] / 64 <= slot (strictly increasing in n).
+__device__ __forceinline__ ChunkPos locate_chunk(long slot, const int32_t *cu, int N, int T) {
+    ChunkPos p;
+    if (!cu) {
+        const int ncs = (T + kChunk - 1) / kChunk;
+        p.n = (int)(slot / ncs);
+        p.c = (int)(slot % ncs);
+        p.tok0 = (long)p.n * T + (long)p.c * kChunk;
+        p.Cc = min(kChunk, T - p.c * kChunk);
+        p.valid = true;
+        return p;
+    }
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((long)mid + cu[mid] / kChunk <= slot) lo = mid; else hi = mid - 1;
+    }
+    p.n = lo;
+    const long s = cu[lo], L = (long)cu[lo + 1] - s;
+    p.c = (int)(slot - (lo + s / kChunk));
+    p.valid = p.c >= 0 && (long)p.c * kChunk < L;
+    p.tok0 = s + (long)p.c * kChunk;
+    p.Cc = p.valid ? (int)min((long)kChunk, L - (long)p.c * kChunk) : 0;
+    return p;
+}
+
+// ------------------------------------------------------------------ kernel 1: chunk-local
+template <bool BF16, int D> struct ChunkSmem {
+    using TIO = typename std::conditional<BF16, uint16_t, float>::type;
+    static constexpr int GS = D + 4, KS = D + 8, VS = kChunk + 8, AS = kChunk + 4;
+    union {
+        float G[kChunk][GS];  // cumulative log2-decay, then
+        float T[kChunk][AS];  // the UT transform Tm
+    } g;
+    union {
+        struct { TIO K[kChunk][KS]; TIO Q[kChunk][KS]; } in;
+        struct { float Akk[kChunk][AS]; float Aqk[kChunk][AS]; } a;
+    } kq;
+    TIO VT[D][VS];            // V transposed: VT[j][t]
+    float bridge[6][D];
+    float beta[kChunk];
+    int flag;
+};
+
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256)
+chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
+                   const typename ChunkSmem<BF16, D>::TIO *__restrict__ k,
+                   const typename ChunkSmem<BF16, D>::TIO *__restrict__ v,
+                   const float *__restrict__ g, const float *__restrict__ beta,
+                   const int32_t *__restrict__ cu, int N, int T, int H, char *__restrict__ ws) {
+    using TIO = typename ChunkSmem<BF16, D>::TIO;
+    using P = Prec<BF16>;
+    using L = WsLayout<BF16, D>;
+    using Plain = typename P::Plain;
+    using Split = typename P::Split;
+    constexpr int NKB = L::NKB, NRT = L::NRT;
+    __shared__ ChunkSmem<BF16, D> sm;
+
+    const long slot = blockIdx.x;
+    const int h = blockIdx.y;
+    const ChunkPos pos = locate_chunk(slot, cu, N, T);
+    if (!pos.valid) return;  // uniform over the block
+    const int Cc = pos.Cc;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    char *wsb = ws + ((size_t)slot * H + h) * L::bytes;
+    const long rowstride = (long)H * D;  // elements between consecutive tokens
+    const long base_in = (pos.tok0 * H + h) * (long)D;
+
+    // ---------------- phase 1: loads (rows >= Cc are zero)
+    if (tid == 0) sm.flag = 0;
+    for (int e = tid; e < kChunk * (D / 4); e += 256) {
+        const int t = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        f32x4 x = zero4();
+        if (t < Cc) x = *reinterpret_cast<const f32x4 *>(g + base_in + t * rowstride + c4);
+        *reinterpret_cast<f32x4 *>(&sm.g.G[t][c4]) = x * kLog2e;
+    }
+    for (int e = tid; e < kChunk * (D / 4); e += 256) {
+        const int t = e / (D / 4), c4 = (e % (D / 4)) * 4;
+        f32x4 kx = zero4(), qx = zero4(), vx = zero4();
+        if (t < Cc) {
+            kx = load4(k + base_in + t * rowstride + c4);
+            qx = load4(q + base_in + t * rowstride + c4);
+            vx = load4(v + base_in + t * rowstride + c4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            IO<TIO>::store(&sm.kq.in.K[t][0], c4 + u, kx[u]);
+            IO<TIO>::store(&sm.kq.in.Q[t][0], c4 + u, qx[u]);
+            IO<TIO>::store(&sm.VT[c4 + u][0], t, vx[u]);
+        }
+    }
+    if (tid < kChunk) sm.beta[tid] = tid < Cc ? beta[(pos.tok0 + tid) * H + h] : 0.f;
+    __syncthreads();
+    if (tid < D) {  // inclusive cumulative sum over the chunk, one channel per thread
+        float run = 0.f;
+        for (int t = 0; t < kChunk; ++t) {
+            run += sm.g.G[t][tid];
+            sm.g.G[t][tid] = run;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- phase 2: element-wise products, written as operand fragments
+    char *wsW = wsb + L::offW, *wsQ = wsb + L::offQ, *wsK = wsb + L::offK, *wsA = wsb + L::offA;
+    float *wsU = reinterpret_cast<float *>(wsb + L::offU);
+    float *wsE = reinterpret_cast<float *>(wsb + L::offE);
+    if (tid < D) wsE[tid] = fast_exp2(sm.g.G[kChunk - 1][tid]);
+    for (int e = tid; e < 6 * D; e += 256) {
+        const int p = e / D, c = e % D;
+        const int I = p < 1 ? 1 : p < 3 ? 2 : 3, J = p - (I - 1) * I / 2;
+        sm.bridge[p][c] = fast_exp2(sm.g.G[mid_row(I)][c] - sm.g.G[mid_row(J)][c]);
+    }
+    bool span_bad = false;
+    Plain Xf[2][2];  // X^T fragments (rows: channel tiles 2kb, 2kb+1; k: token blocks) kept for W
+    for (int kb = wave; kb < NKB; kb += 4) {
+        // Qh = Q e^G, as A fragments (row t, k = channel)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = 16 * tt + r16, m = mid_row(tt);
+            float vals[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const int c = 32 * kb + kslot(grp, s);
+                const float gt = sm.g.G[t][c];
+                span_bad |= fabsf(gt - sm.g.G[m][c]) > 115.f;
+                vals[s] = IO<TIO>::load(&sm.kq.in.Q[t][0], c) * fast_exp2(gt);
+            }
+            P::st_plain(wsQ, L::nQ, tt * NKB + kb, lane, P::plain(vals));
+        }
+        // Kh^T = (K e^{gamma - G})^T and X^T = (K e^G)^T, as A fragments (row channel, k = token)
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int rt = 2 * kb + r2, i = 16 * rt + r16;
+            const float gam = sm.g.G[kChunk - 1][i];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                float kh[8], xv[8];
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int t = 32 * kb2 + kslot(grp, s);
+                    const float gt = sm.g.G[t][i];
+                    const float kv = IO<TIO>::load(&sm.kq.in.K[t][0], i);
+                    kh[s] = kv * fast_exp2(gam - gt);
+                    xv[s] = kv * fast_exp2(gt);
+                }
+                P::st_plain(wsK, L::nK, rt * 2 + kb2, lane, P::plain(kh));
+                Xf[r2][kb2] = P::plain(xv);
+            }
+        }
+    }
+    if (span_bad) atomicOr(&sm.flag, 1);
+    __syncthreads();
+
+    // ---------------- phase 3: decayed Gram matrices Akk, Aqk
+    const bool fallback = sm.flag != 0;
+    if (!fallback) {
+        f32x4 accK[10], accQ[10];
+#pragma unroll
+        for (int p = 0; p < 10; ++p) { accK[p] = zero4(); accQ[p] = zero4(); }
+        const bool has_work = wave < NKB;
+        if (has_work) {
+            for (int kb = wave; kb < NKB; kb += 4) {
+                float kA[4][8], qA[4][8], kB[4][8];
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    const int i = 16 * I + r16, m = mid_row(I);
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const int c = 32 * kb + kslot(grp, s);
+                        const float d = sm.g.G[i][c] - sm.g.G[m][c];
+                        const float kv = IO<TIO>::load(&sm.kq.in.K[i][0], c);
+                        const float qv = IO<TIO>::load(&sm.kq.in.Q[i][0], c);
+                        const float fa = fast_exp2(d), fb = fast_exp2(-d);
+                        kA[I][s] = kv * fa;
+                        qA[I][s] = qv * fa;
+                        kB[I][s] = kv * fb;
+                    }
+                }
+                Split Bop[4];
+#pragma unroll
+                for (int J = 0; J < 4; ++J) Bop[J] = P::split(kB[J]);
+#pragma unroll
+                for (int p = 0; p < 10; ++p) {
+                    int I, J;
+                    pair_ij(p, I, J);
+                    float ak[8], aq[8];
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        float br = 1.f;
+                        if (I > J) br = sm.bridge[bridge_idx(I, J)][32 * kb + kslot(grp, s)];
+                        ak[s] = kA[I][s] * br;
+                        aq[s] = qA[I][s] * br;
+                    }
+                    accK[p] = mfma(P::split(ak), Bop[J], accK[p]);
+                    accQ[p] = mfma(P::split(aq), Bop[J], accQ[p]);
+                }
+            }
+        }
+        __syncthreads();  // every wave is done reading K, Q (aliased by Akk, Aqk below)
+        const int nw = NKB < 4 ? NKB : 4;
+        for (int r = 0; r < nw; ++r) {
+            if (wave == r) {
+#pragma unroll
+                for (int p = 0; p < 10; ++p) {
+                    int I, J;
+                    pair_ij(p, I, J);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = 16 * I + 4 * grp + e, col = 16 * J + r16;
+                        if (r == 0) {
+                            sm.kq.a.Akk[row][col] = accK[p][e];
+                            sm.kq.a.Aqk[row][col] = accQ[p][e];
+                        } else {
+                            sm.kq.a.Akk[row][col] += accK[p][e];
+                            sm.kq.a.Aqk[row][col] += accQ[p][e];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    } else {
+        // exact element-wise fallback for extreme decay inside a 16-token sub-block
+        float rk[16], rq[16];
+        const int i = tid >> 2, j0 = (tid & 3) * 16;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int j = j0 + jj;
+            float ak = 0.f, aq = 0.f;
+            if (j <= i) {
+                for (int c = 0; c < D; ++c) {
+                    const float e = fast_exp2(sm.g.G[i][c] - sm.g.G[j][c]);
+                    const float kj = IO<TIO>::load(&sm.kq.in.K[j][0], c);
+                    ak += IO<TIO>::load(&sm.kq.in.K[i][0], c) * kj * e;
+                    aq += IO<TIO>::load(&sm.kq.in.Q[i][0], c) * kj * e;
+                }
+            }
+            rk[jj] = ak;
+            rq[jj] = aq;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            sm.kq.a.Akk[i][j0 + jj] = rk[jj];
+            sm.kq.a.Aqk[i][j0 + jj] = rq[jj];
+        }
+        __syncthreads();
+    }
+    // beta rows and the causal masks (also clears never-written upper blocks)
+    for (int e = tid; e < kChunk * kChunk; e += 256) {
+        const int i = e >> 6, j = e & 63;
+        const float a = sm.kq.a.Akk[i][j], b = sm.kq.a.Aqk[i][j];
+        sm.kq.a.Akk[i][j] = j < i ? sm.beta[i] * a : 0.f;
+        sm.kq.a.Aqk[i][j] = j <= i ? b : 0.f;
+        sm.g.T[i][j] = (j >> 4) > (i >> 4) ? 0.f : sm.g.T[i][j];
+    }
+    __syncthreads();
+
+    // ---------------- phase 4: Tm = (I + Akk)^-1 (unit lower triangular), fp32
+    if (wave == 0) {  // 16x16 diagonal blocks: lane owns column j of block b
+        const int b = lane >> 4, j = lane & 15;
+        float tc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc += sm.kq.a.Akk[16 * b + i][16 * b + m] * tc[m];
+            tc[i] = i == j ? 1.f : (i < j ? 0.f : -acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.g.T[16 * b + i][16 * b + j] = tc[i];
+    }
+    __syncthreads();
+    for (int I = 1; I < 4; ++I) {  // block rows: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
+        const int J = wave;
+        if (J < I) {
+            f32x4 x = zero4();
+            for (int M = J; M < I; ++M) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.kq.a.Akk[16 * I + r16][16 * M + 4 * grp + s],
+                                                             sm.g.T[16 * M + 4 * grp + s][16 * J + r16], x, 0, 0, 0);
+            }
+            f32x4 y = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.g.T[16 * I + r16][16 * I + 4 * grp + s], x[s], y, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.g.T[16 * I + 4 * grp + e][16 * J + r16] = -y[e];
+        }
+        __syncthreads();
+    }
+
+    // ---------------- phase 5: W = T' X, U = T' V, Aqk fragments
+    // T' = Tm Diag(beta) fragments; the same values serve as the A operand (row t, k = t')
+    // of U and as the B operand (k = t', column t) of W^T.
+    Split Tf[6];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
+        float vals[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int tp = 32 * kb2 + kslot(grp, s);
+            vals[s] = sm.g.T[16 * tt + r16][tp] * sm.beta[tp];
+        }
+        Tf[f] = P::split(vals);
+    }
+    for (int kb = wave; kb < NKB; kb += 4) {  // W fragments (tt, kb)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc[r2] = mfma(Xf[r2][kb2], Tf[aidx(tt, kb2)], acc[r2]);
+            float vals[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+            P::st_plain(wsW, L::nW, tt * NKB + kb, lane, P::plain(vals));
+        }
+    }
+    for (int jt = wave; jt < NRT; jt += 4) {  // U tiles (jt, tt)
+        Plain Vf[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            float vals[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s) vals[s] = IO<TIO>::load(&sm.VT[16 * jt + r16][0], 32 * kb2 + kslot(grp, s));
+            Vf[kb2] = P::plain(vals);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc = mfma(Tf[aidx(tt, kb2)], Vf[kb2], acc);
+            reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
+        }
+    }
+    for (int f = wave; f < 6; f += 4) {  // Aqk fragments
+        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
+        float vals[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) vals[s] = sm.kq.a.Aqk[16 * tt + r16][32 * kb2 + kslot(grp, s)];
+        P::st_split(wsA, L::nA, f, lane, P::split(vals));
+    }
+}
+
+// ------------------------------------------------------------------ kernel 2: state scan
+template <bool BF16, int D>
+__global__ void __launch_bounds__(64)
+chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
+                  const float *__restrict__ s0, float *__restrict__ sN,
+                  typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws) {
+    using TIO = typename ChunkSmem<BF16, D>::TIO;
+    using P = Prec<BF16>;
+    using L = WsLayout<BF16, D>;
+    using Split = typename P::Split;
+    constexpr int NKB = L::NKB, NRT = L::NRT, NJT = D / 16;
+    // the NJT column tiles of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
+    const int b = blockIdx.x, xcd = b & 7, sl = b >> 3;
+    const int jt = sl % NJT, chain = (sl / NJT) * 8 + xcd;
+    if (chain >= nchains) return;
+    const int n = chain / H, h = chain % H;
+    const int lane = threadIdx.x, grp = lane >> 4, r16 = lane & 15;
+    const int col = 16 * jt + r16;
+
+    long s_tok, L_n, slot0;
+    if (cu) {
+        s_tok = cu[n];
+        L_n = (long)cu[n + 1] - s_tok;
+        slot0 = n + s_tok / kChunk;
+    } else {
+        s_tok = (long)n * T;
+        L_n = T;
+        slot0 = (long)n * ((T + kChunk - 1) / kChunk);
+    }
+    const long nck = (L_n + kChunk - 1) / kChunk;
+
+    f32x4 S[NRT];
+    const long sbase = (long)chain * D * D;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[rt][e] = s0 ? s0[sbase + (long)(16 * rt + 4 * grp + e) * D + col] : 0.f;
+
+    for (long c = 0; c < nck; ++c) {
+        const char *wsb = ws + ((size_t)(slot0 + c) * H + h) * L::bytes;
+        const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
+        const long tok0 = s_tok + c * kChunk;
+        Split Sop[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            float vals[8] = {S[2 * kb][0], S[2 * kb][1], S[2 * kb][2], S[2 * kb][3],
+                             S[2 * kb + 1][0], S[2 * kb + 1][1], S[2 * kb + 1][2], S[2 * kb + 1][3]};
+            Sop[kb] = P::split(vals);
+        }
+        f32x4 ud[4], oacc[4];
+        const f32x4 *wsU = reinterpret_cast<const f32x4 *>(wsb + L::offU);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 ws_acc = zero4(), oa = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                ws_acc = mfma(P::ld_plain(wsb + L::offW, L::nW, tt * NKB + kb, lane), Sop[kb], ws_acc);
+                oa = mfma(P::ld_plain(wsb + L::offQ, L::nQ, tt * NKB + kb, lane), Sop[kb], oa);
+            }
+            ud[tt] = wsU[(jt * 4 + tt) * 64 + lane] - ws_acc;
+            oacc[tt] = oa;
+        }
+        Split Uop[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            float vals[8] = {ud[2 * kb2][0], ud[2 * kb2][1], ud[2 * kb2][2], ud[2 * kb2][3],
+                             ud[2 * kb2 + 1][0], ud[2 * kb2 + 1][1], ud[2 * kb2 + 1][2], ud[2 * kb2 + 1][3]};
+            Uop[kb2] = P::split(vals);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+#pragma unroll
+            for (int kb2 = 0; kb2 <= tt / 2; ++kb2)
+                oacc[tt] = mfma(P::ld_split(wsb + L::offA, L::nA, aidx(tt, kb2), lane), Uop[kb2], oacc[tt]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tt + 4 * grp + e;
+                if (t < Cc) IO<TIO>::store(o, ((tok0 + t) * H + h) * (long)D + col, scale * oacc[tt][e]);
+            }
+        }
+        const float *wsE = reinterpret_cast<const float *>(wsb + L::offE);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(wsE + 16 * rt + 4 * grp);
+            f32x4 acc = S[rt] * eg;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+                acc = mfma(P::ld_plain(wsb + L::offK, L::nK, rt * 2 + kb2, lane), Uop[kb2], acc);
+            S[rt] = acc;
+        }
+    }
+    if (sN) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sN[sbase + (long)(16 * rt + 4 * grp + e) * D + col] = S[rt][e];
+    }
+}
+
+// ------------------------------------------------------------------ host side
+size_t fwd_bytes_per_chunk_head(bool bf16, int d) {
+    if (bf16) return d == 128 ? WsLayout<true, 128>::bytes : WsLayout<true, 64>::bytes;
+    return d == 128 ? WsLayout<false, 128>::bytes : WsLayout<false, 64>::bytes;
+}
+
+long fwd_chunk_slots(int B, int T, int N, bool varlen) {
+    const long ncs = ((long)T + kChunk - 1) / kChunk;
+    return varlen ? (long)N + ncs : (long)B * ncs;
+}
+
+template <bool BF16, int D>
+static hipError_t launch_local_t(const FwdArgs &a, hipStream_t st) {
+    using TIO = typename ChunkSmem<BF16, D>::TIO;
+    const long slots = fwd_chunk_slots(a.B, a.T, a.N, a.cu_seqlens != nullptr);
+    if (slots <= 0 || a.H <= 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_local_kernel<BF16, D>), dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, st,
+                       (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T,
+                       a.H, static_cast<char *>(a.ws));
+    return hipGetLastError();
+}
+
+template <bool BF16, int D>
+static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
+    using TIO = typename ChunkSmem<BF16, D>::TIO;
+    const int nchains = a.N * a.H;
+    if (nchains <= 0) return hipSuccess;
+    const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16);
+    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D>), dim3((unsigned)blocks), dim3(64), 0, st, a.cu_seqlens, a.N,
+                       a.T, a.H, nchains, a.scale, a.s0, a.sN, (TIO *)a.o, (const char *)a.ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {
+    if (a.bf16) return a.dk == 128 ? launch_local_t<true, 128>(a, st) : launch_local_t<true, 64>(a, st);
+    return a.dk == 128 ? launch_local_t<false, 128>(a, st) : launch_local_t<false, 64>(a, st);
+}
+
+hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st) {
+    if (a.bf16) return a.dk == 128 ? launch_scan_t<true, 128>(a, st) : launch_scan_t<true, 64>(a, st);
+    return a.dk == 128 ? launch_scan_t<false, 128>(a, st) : launch_scan_t<false, 64>(a, st);
+}
+
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t st) {
+    hipError_t e = launch_fwd_local(a, st);
+    return e != hipSuccess ? e : launch_fwd_scan(a, st);
+}
+
+}  // namespace kda

@@ -1,0 +1,50 @@
+// kda_internal.h -- launcher interface between the C ABI (kda_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    bool bf16;
+    int N, H, dk, dv;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float scale;
+    float *state;
+    void *o;
+};
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+
+struct PrepArgs {
+    bool bf16;
+    int B, T, H, d, W, N;
+    const int32_t *cu_seqlens;  // NULL: dense rows
+    const void *x;
+    const float *w;
+    void *y;
+};
+hipError_t launch_prep(const PrepArgs &a, hipStream_t st);
+
+struct FwdArgs {
+    bool bf16;
+    int B, T, H, dk, dv, N;
+    const int32_t *cu_seqlens;  // NULL: dense
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float scale;
+    const float *s0;
+    float *sN;
+    void *o;
+    void *ws;
+};
+// Bytes of workspace for one (chunk, head) and the number of chunk slots.
+size_t fwd_bytes_per_chunk_head(bool bf16, int d);
+long fwd_chunk_slots(int B, int T, int N, bool varlen);
+hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);          // both phases
+hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st);    // chunk-local phase
+hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st);     // state-scan phase
+
+}  // namespace kda

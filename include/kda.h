@@ -1,0 +1,156 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention operator library (libkda.so).
+ *
+ * The operator (one sequence n, one head h, tokens t = 1..L):
+ *     S~  = Diag(alpha_t) S_{t-1},            alpha_t = exp(g_t) in (0,1]^{d_k}
+ *     S_t = S~ + beta_t k_t (v_t - S~^T k_t)^T
+ *     o_t = scale * S_t^T q_t
+ * Sources: course page "线性注意力与 KDA" (ai.air7.fun, Day 19), section 3 (decay per
+ * channel, then the delta write of the prediction error) and section 2 (read-out
+ * o_t = q_t S_t with a fixed d_k x d_v state); page "Kimi K3 注意力三件套"
+ * (yeyulingfeng.com), KDA section (alpha_t is a vector over the d_k channels; q and k
+ * pass a short causal convolution and an L2 norm; deployment uses a chunkwise form);
+ * blog post ciyuanerhao.com post-114, chapter 3 (state passed in as a cache that
+ * defaults to zero; DeltaNet code in [d_k, d_v] orientation) and chapter 4
+ * (alpha of shape (B, T, C) multiplying the rows of S).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major buffers,
+ *     16-byte aligned.  The caller owns all memory, including the workspace; the
+ *     library never allocates, frees or keeps device memory, keeps no global
+ *     state and may be called concurrently on different streams.
+ *   - io dtype (KDA_F32 or KDA_BF16) applies to q, k, v, o and to x, y of kda_prep.
+ *     g (= log alpha), beta, conv weights and states are always fp32.
+ *   - State layout [N, H, d_k, d_v] fp32, K-major: element (i, j) couples key
+ *     channel i with value channel j, so o = S^T q.
+ *   - Host-checkable arguments are validated before anything is launched; on
+ *     error a status is returned and no output is touched.  Device contents
+ *     (finite inputs, monotone cu_seqlens) are the caller's contract; NaN and Inf
+ *     propagate.  g must be finite (g = -inf, a hard reset, is not supported).
+ *   - Work is enqueued on `stream` and the call returns without synchronising.
+ *     Kernel faults surface at the caller's next synchronisation.  No float
+ *     atomics are used: results are bitwise reproducible on one device.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned buffer, bad dtype */
+    KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k not in {64, 128}) */
+    KDA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than kda_fwd_workspace_bytes */
+    KDA_ERR_LAUNCH = 4            /* the HIP runtime rejected a kernel launch */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *kda_status_string(kda_status_t status);
+
+/*
+ * Workspace needed by kda_fwd for these sizes (bytes, a multiple of 256).
+ * varlen != 0 means cu_seqlens will be passed; then B must be 1 and T is the packed
+ * token count.  Returns 0 for unsupported or invalid sizes.
+ */
+size_t kda_fwd_workspace_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                               int N, int varlen);
+
+/*
+ * kda_fwd -- chunked prefill over a dense batch or a packed (varlen) batch.
+ * Computes exactly the recurrence above for every sequence and head, with the chunkwise
+ * parallel form (chunks of 64 tokens restarting at each sequence start) that the
+ * yeyulingfeng page's KDA section names and the post-114 blog's chapter 3 describes
+ * (parallel inside a chunk, serial across chunks).
+ *
+ *   io            KDA_F32 or KDA_BF16 (dtype of q, k, v, o)
+ *   B, T, H       dense: B sequences of T tokens each; varlen: B = 1, T = cu_seqlens[N]
+ *   d_k, d_v      head sizes; supported: d_k == d_v in {64, 128}
+ *   cu_seqlens    NULL for dense; else device int32 [N + 1], cu_seqlens[0] = 0,
+ *                 non-decreasing, cu_seqlens[N] = T (zero-length sequences allowed)
+ *   N             number of sequences (dense: must equal B)
+ *   q, k          [B, T, H, d_k] io dtype (q and k are expected L2-normalised per head)
+ *   v             [B, T, H, d_v] io dtype
+ *   g             [B, T, H, d_k] fp32, log of the per-channel forget gate (finite, <= 0)
+ *   beta          [B, T, H] fp32, write strength
+ *   scale         multiplies the read-out
+ *   initial_state [N, H, d_k, d_v] fp32 or NULL (zero state)
+ *   final_state   [N, H, d_k, d_v] fp32 or NULL (not written); may alias initial_state
+ *   o             [B, T, H, d_v] io dtype, written for every token; must not alias inputs
+ *   workspace     device buffer of at least kda_fwd_workspace_bytes(...) bytes
+ */
+kda_status_t kda_fwd(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                     const int32_t *cu_seqlens, int N,
+                     const void *q, const void *k, const void *v,
+                     const float *g, const float *beta, float scale,
+                     const float *initial_state, float *final_state,
+                     void *o, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/*
+ * The two phases of kda_fwd, for callers that schedule or time them separately.
+ * kda_fwd(...) is exactly kda_fwd_chunk_local(...) followed by kda_fwd_state_scan(...) on the
+ * same stream with the same workspace; arguments have the meaning given for kda_fwd.
+ *   kda_fwd_chunk_local: per (chunk, head), fully parallel -- cumulative log-decay, decayed
+ *     Gram matrices, the UT transform of the chunk and the WY factors; results go to the
+ *     workspace only.
+ *   kda_fwd_state_scan: per (sequence, head), serial over the chunks -- propagates the state,
+ *     writes o and final_state.  Reads what kda_fwd_chunk_local left in the workspace.
+ */
+kda_status_t kda_fwd_chunk_local(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                 const int32_t *cu_seqlens, int N,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+kda_status_t kda_fwd_state_scan(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                const int32_t *cu_seqlens, int N, float scale,
+                                const float *initial_state, float *final_state, void *o,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_decode_step -- one token of the recurrence for N independent sequences, in place.
+ * The state stays resident in HBM; each call reads and rewrites it once
+ * (the fixed-size state of the course page's section 2 makes each step O(1) in the
+ * context length).
+ *
+ *   q, k   [N, H, d_k] io dtype;  v [N, H, d_v] io dtype
+ *   g      [N, H, d_k] fp32 (log alpha);  beta [N, H] fp32
+ *   state  [N, H, d_k, d_v] fp32, read then overwritten with the updated state
+ *   o      [N, H, d_v] io dtype (read-out with the updated state)
+ *   Supported: d_k, d_v in {64, 128}.
+ */
+kda_status_t kda_decode_step(kda_dtype_t io, int N, int H, int d_k, int d_v,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, float scale,
+                             float *state, void *o, hipStream_t stream);
+
+/*
+ * kda_prep -- q/k prologue: short causal depthwise convolution, SiLU, L2 norm per head.
+ * (yeyulingfeng page, KDA section: short causal convolution then L2 normalisation;
+ * post-114 blog chapter 3: normalize(silu(.)).)  Called once for q and once for k.
+ *     c' = sum_{tau=0}^{W-1} conv_w[c, tau] * x_{t-(W-1)+tau}[c]   (x = 0 before the
+ *          first token of the sequence; tap W-1 is the current token; no bias)
+ *     y  = silu(c') / max(||silu(c')||_2 over the d channels of the head, 1e-12)
+ *
+ *   x, y        [B, T, H, d] io dtype (y must not alias x)
+ *   cu_seqlens  NULL (each of the B rows is one sequence) or device int32 [N + 1] with B = 1
+ *   conv_w      [H * d, W] fp32 device buffer;  W in 1..8
+ *   Supported: d in {64, 128}.
+ */
+kda_status_t kda_prep(kda_dtype_t io, int B, int T, int H, int d,
+                      const int32_t *cu_seqlens, int N,
+                      const void *x, const float *conv_w, int W, void *y,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

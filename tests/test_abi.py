@@ -1,0 +1,110 @@
+"""C ABI contract checks that need no GPU: the library loads, exports what include/kda.h
+declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_93_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.lib()
+    names = declared_functions()
+    assert {"kda_fwd", "kda_decode_step", "kda_prep", "kda_fwd_workspace_bytes", "kda_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(5):
+        s = kda.status_string(code)
+        assert s.startswith("KDA_")
+    assert "unknown" in kda.status_string(99)
+
+
+def test_workspace_bytes():
+    b = kda.fwd_workspace_bytes(kda.KDA_BF16, 4, 4096, 16, 128, 128, 4, False)
+    assert b > 0 and b % 256 == 0
+    assert b == 4 * 64 * 16 * kda.fwd_workspace_bytes(kda.KDA_BF16, 1, 64, 1, 128, 128, 1, False)
+    # varlen: one extra slot per sequence
+    v = kda.fwd_workspace_bytes(kda.KDA_BF16, 1, 4096, 16, 128, 128, 3, True)
+    assert v == (64 + 3) * 16 * kda.fwd_workspace_bytes(kda.KDA_BF16, 1, 64, 1, 128, 128, 1, False)
+    assert kda.fwd_workspace_bytes(kda.KDA_BF16, 1, 64, 1, 96, 96, 1, False) == 0       # unsupported d
+    assert kda.fwd_workspace_bytes(kda.KDA_BF16, 1, 64, 1, 128, 64, 1, False) == 0      # d_k != d_v
+    assert kda.fwd_workspace_bytes(kda.KDA_BF16, 2, 64, 1, 128, 128, 2, True) == 0      # varlen needs B = 1
+    assert kda.fwd_workspace_bytes(7, 1, 64, 1, 128, 128, 1, False) == 0                # bad dtype
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd_call(**over):
+    a = dict(io=kda.KDA_BF16, B=1, T=64, H=1, dk=128, dv=128, cu=None, N=1, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+             beta=FAKE, scale=1.0, s0=None, sN=None, o=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return kda.lib().kda_fwd(a["io"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["cu"], a["N"], a["q"], a["k"],
+                             a["v"], a["g"], a["beta"], a["scale"], a["s0"], a["sN"], a["o"], a["ws"], a["wsb"],
+                             a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(io=5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARGUMENT),                      # dense: N must equal B
+    (dict(q=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(o=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(k=FAKE + 4), kda.KDA_ERR_INVALID_ARGUMENT),              # misaligned
+    (dict(s0=FAKE + 8), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(cu=FAKE, B=2, N=2), kda.KDA_ERR_INVALID_ARGUMENT),       # varlen needs B = 1
+    (dict(dk=96, dv=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(ws=None), kda.KDA_ERR_WORKSPACE),
+    (dict(wsb=1024), kda.KDA_ERR_WORKSPACE),
+])
+def test_fwd_rejects(over, code):
+    assert fwd_call(**over) == code
+
+
+def test_fwd_empty_problem_is_ok_without_launch():
+    assert fwd_call(H=0, ws=None, wsb=0) == kda.KDA_OK
+    assert fwd_call(B=0, N=0, T=0, ws=None, wsb=0) == kda.KDA_OK
+
+
+def test_decode_and_prep_reject():
+    L = kda.lib()
+    assert L.kda_decode_step(kda.KDA_BF16, 1, 1, 96, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, FAKE, FAKE, None) \
+        == kda.KDA_ERR_UNSUPPORTED
+    assert L.kda_decode_step(kda.KDA_BF16, 1, 1, 128, 128, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, None, FAKE, None) \
+        == kda.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_decode_step(kda.KDA_BF16, 1, 1, 128, 128, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 1.0, FAKE, FAKE,
+                             None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_decode_step(kda.KDA_BF16, 0, 1, 128, 128, None, None, None, None, None, 1.0, None, None, None) \
+        == kda.KDA_OK
+    assert L.kda_prep(kda.KDA_BF16, 1, 8, 1, 128, None, 1, FAKE, FAKE, 0, FAKE + 16, None) \
+        == kda.KDA_ERR_INVALID_ARGUMENT                             # W = 0
+    assert L.kda_prep(kda.KDA_BF16, 1, 8, 1, 128, None, 1, FAKE, FAKE, 9, FAKE + 16, None) \
+        == kda.KDA_ERR_UNSUPPORTED                                  # W > 8
+    assert L.kda_prep(kda.KDA_BF16, 1, 8, 1, 100, None, 1, FAKE, FAKE, 4, FAKE + 16, None) \
+        == kda.KDA_ERR_UNSUPPORTED
+    assert L.kda_prep(kda.KDA_BF16, 1, 8, 1, 128, None, 1, FAKE, FAKE, 4, FAKE, None) \
+        == kda.KDA_ERR_INVALID_ARGUMENT                             # y aliases x
+    assert L.kda_prep(kda.KDA_BF16, 2, 8, 1, 128, FAKE, 2, FAKE, FAKE, 4, FAKE + 16, None) \
+        == kda.KDA_ERR_INVALID_ARGUMENT                             # varlen with B != 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(kda, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        kda.lib()

@@ -1,0 +1,93 @@
+"""kda_decode_step against the fp64 oracle (GPU, through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_93_amd as kda
+import kda_inputs as ki
+import oracle
+from gpu_util import DEV, dev_f32, dev_io, err, host, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_config3_sampled_chains():
+    """256 sequences x 32 heads, d = 128, bf16 tokens, fp32 state in HBM, 100 steps.
+    All heads run on the GPU; 48 sampled (sequence, head) chains are checked step by step."""
+    c = ki.CONFIG3
+    N, H, d, steps, seed = c["N"], c["H"], c["d"], c["steps"], c["seed"]
+    S0 = ki.decode_initial_state(N, H, d, seed)
+    state = dev_f32(S0)
+    rng = np.random.default_rng(1)
+    picks = [(int(n), int(h)) for n, h in zip(rng.integers(0, N, 48), rng.integers(0, H, 48))]
+    hist = {nh: {"q": [], "k": [], "v": [], "g": [], "b": [], "o": []} for nh in picks}
+    for s in range(steps):
+        q, k, v, g, beta = ki.decode_step_inputs(N, H, d, "bf16", seed, s)
+        o = kda.decode_step(dev_io(q, "bf16"), dev_io(k, "bf16"), dev_io(v, "bf16"), dev_f32(g), dev_f32(beta),
+                            state)
+        oh = host(o)
+        for (n, h) in picks:
+            rec = hist[(n, h)]
+            rec["q"].append(q[n, h]); rec["k"].append(k[n, h]); rec["v"].append(v[n, h])
+            rec["g"].append(g[n, h]); rec["b"].append(beta[n, h]); rec["o"].append(oh[n, h])
+    S_gpu = host(state)
+    worst_o = worst_s = 0.0
+    for (n, h), rec in hist.items():
+        o_ref, S_ref = oracle.chain(np.stack(rec["q"]), np.stack(rec["k"]), np.stack(rec["v"]),
+                                    np.stack(rec["g"]), np.array(rec["b"]), 1.0, S0[n, h])
+        worst_o = max(worst_o, err(np.stack(rec["o"]), o_ref, "bf16"))
+        worst_s = max(worst_s, err(S_gpu[n, h], S_ref, "bf16"))
+    print(f"decode config3: o err {worst_o:.3e}, state err {worst_s:.3e}")
+    assert worst_o <= tol("bf16") and worst_s <= tol("bf16")
+
+
+def test_decode_fp32_equals_recurrence_config0():
+    """Config 0 (fp32, d = 64, T = 256) run as 256 consecutive decode steps."""
+    inp = ki.config0()
+    o_ref, S_ref = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+    state = torch.zeros((1, inp.H, 64, 64), dtype=torch.float32, device=DEV)
+    outs = []
+    for t in range(inp.T):
+        o = kda.decode_step(dev_io(inp.q[:, t], "f32"), dev_io(inp.k[:, t], "f32"), dev_io(inp.v[:, t], "f32"),
+                            dev_f32(inp.g[:, t]), dev_f32(inp.beta[:, t]), state)
+        outs.append(host(o))
+    o_gpu = np.stack(outs, axis=1)
+    e_o, e_s = err(o_gpu, o_ref, "f32"), err(host(state), S_ref, "f32")
+    print(f"decode config0 fp32: o err {e_o:.3e}, state err {e_s:.3e}")
+    assert e_o <= tol("f32") and e_s <= tol("f32")
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64), (64, 64), (128, 128)])
+def test_decode_shapes_fp32(dk, dv):
+    N, H, steps = 3, 2, 6
+    rng = np.random.default_rng(dk + dv)
+    S0 = (rng.standard_normal((N, H, dk, dv)) * 0.1).astype(np.float32)
+    state = dev_f32(S0)
+    toks = [ki.draw_tokens(np.random.default_rng([7, s]), (N,), H, dk, dv, "f32") for s in range(steps)]
+    outs = []
+    for (q, k, v, beta, g) in toks:
+        outs.append(host(kda.decode_step(dev_f32(q), dev_f32(k), dev_f32(v), dev_f32(g), dev_f32(beta), state,
+                                         scale=0.5)))
+    S_gpu = host(state)
+    for n in range(N):
+        for h in range(H):
+            st = lambda i: np.stack([t[i][n, h] for t in toks])
+            o_ref, S_ref = oracle.chain(st(0), st(1), st(2), st(4), np.array([t[3][n, h] for t in toks]), 0.5,
+                                        S0[n, h])
+            assert err(np.stack([o[n, h] for o in outs]), o_ref, "f32") <= tol("f32")
+            assert err(S_gpu[n, h], S_ref, "f32") <= tol("f32")
+
+
+def test_decode_recall_on_gpu():
+    """Unit key and beta = 1: after the step the state maps k to v (S^T k = v), read with q = k."""
+    N, H, d = 4, 3, 128
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((N, H, d))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = rng.standard_normal((N, H, d)).astype(np.float32)
+    g = (-rng.uniform(0, 3, (N, H, d))).astype(np.float32)
+    state = dev_f32(rng.standard_normal((N, H, d, d)).astype(np.float32))
+    o = kda.decode_step(dev_f32(k), dev_f32(k), dev_f32(v), dev_f32(g), dev_f32(np.ones((N, H), np.float32)), state)
+    res = np.max(np.abs(host(o) - v)) / np.max(np.abs(v))
+    print(f"recall residual {res:.2e}")
+    assert res <= 1e-5

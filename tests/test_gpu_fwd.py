@@ -1,0 +1,123 @@
+"""kda_fwd (chunked prefill) against the fp64 oracle (GPU, through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_93_amd as kda
+import kda_inputs as ki
+import oracle
+from gpu_util import DEV, dev_f32, err, host, tol, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def run_and_check(inp: ki.KDAInputs, scale=1.0, chains=None, label=""):
+    q, k, v, g, beta, S0, cu = upload(inp)
+    o, S = kda.fwd(q, k, v, g, beta, scale, S0, cu)
+    torch.cuda.synchronize()
+    R = oracle.Recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, scale, inp.S0, inp.cu_seqlens)
+    res = R.run(chains)
+    worst_o = worst_s = 0.0
+    for (n, h), (o_ref, S_ref) in res.items():
+        b, s, L = R.bounds(n)
+        if L:
+            worst_o = max(worst_o, err(host(o[b, s:s + L, h]), o_ref, inp.io))
+        worst_s = max(worst_s, err(host(S[n, h]), S_ref, inp.io))
+    print(f"fwd {label}: o err {worst_o:.3e}, state err {worst_s:.3e}")
+    assert worst_o <= tol(inp.io), (label, worst_o)
+    assert worst_s <= tol(inp.io), (label, worst_s)
+    return o, S
+
+
+def test_fwd_config0_fp32():
+    """B=1, H=2, T=256, d=64, fp32, S0 = 0 (gate 1e-4)."""
+    run_and_check(ki.config0(), label="config0")
+
+
+def test_fwd_small_bf16_ragged():
+    """Several chunks and a ragged tail (T = 200), random initial state, scale != 1."""
+    run_and_check(ki.make_dense(2, 200, 3, 128, 128, "bf16", 11, s0_std=0.5), scale=0.7, label="ragged")
+
+
+@pytest.mark.parametrize("io,d", [("f32", 128), ("bf16", 64), ("f32", 64)])
+def test_fwd_other_dtypes_and_sizes(io, d):
+    run_and_check(ki.make_dense(2, 150, 2, d, d, io, 12 + d, s0_std=0.3), label=f"{io} d={d}")
+
+
+def test_fwd_config1_full():
+    """B=4, H=16, T=4096, d=128, bf16 q/k/v, fp32 g/beta/state, S0 = 0: every chain checked."""
+    run_and_check(ki.config1(), label="config1")
+
+
+@pytest.mark.parametrize("variant", ["weak_decay", "alpha_one", "scalar_alpha"])
+def test_fwd_long_memory_variants(variant):
+    """Decay regimes that exercise state propagation across many chunks."""
+    inp = ki.make_dense(1, 2048, 4, 128, 128, "bf16", 21, s0_std=0.02,
+                        g_shift=-5.0 if variant == "weak_decay" else 2.0)
+    if variant == "alpha_one":
+        inp.g[:] = 0.0
+    if variant == "scalar_alpha":
+        inp.g[:] = inp.g[..., :1]
+    run_and_check(inp, label=variant)
+
+
+def test_fwd_varlen_edges():
+    """Packed batch with empty, 1-token, chunk-edge and multi-chunk sequences and per-sequence states."""
+    inp = ki.make_varlen([1, 63, 64, 65, 0, 130, 7, 300, 128], 2, 128, 128, "bf16", 31, s0_std=0.3)
+    run_and_check(inp, label="varlen")
+
+
+def test_fwd_no_initial_state_no_final_state():
+    inp = ki.make_dense(1, 100, 2, 128, 128, "bf16", 41)
+    q, k, v, g, beta, _, _ = upload(inp)
+    o, S = kda.fwd(q, k, v, g, beta, output_final_state=False)
+    assert S is None
+    o_ref, _ = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+    assert err(host(o), o_ref, "bf16") <= tol("bf16")
+
+
+def test_fwd_extreme_decay_fallback():
+    """Log-decay of ~90 nats inside a 16-token sub-block forces the exact element-wise Gram path."""
+    inp = ki.make_dense(1, 192, 2, 128, 128, "bf16", 51, s0_std=0.3)
+    inp.g[0, 70:73, :, :17] = -30.0      # channels 0..16, three tokens: 90 nats
+    inp.g[0, 140, 1, 5] = -200.0
+    run_and_check(inp, label="fallback")
+
+
+def test_fwd_deterministic():
+    inp = ki.make_dense(2, 300, 3, 128, 128, "bf16", 61, s0_std=0.1)
+    args = upload(inp)
+    o1, S1 = kda.fwd(*args[:5], 1.0, args[5])
+    o2, S2 = kda.fwd(*args[:5], 1.0, args[5])
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_fwd_state_resume_and_aliasing():
+    """fwd over T1 + T2 equals fwd over T2 started from the final state of T1 (states aliased in place)."""
+    inp = ki.make_dense(1, 320, 2, 128, 128, "bf16", 71, s0_std=0.1)
+    q, k, v, g, beta, S0, _ = upload(inp)
+    o_full, S_full = kda.fwd(q, k, v, g, beta, 1.0, S0)
+    st = S0.clone()
+    T1 = 100
+    o1, _ = kda.fwd(q[:, :T1].contiguous(), k[:, :T1].contiguous(), v[:, :T1].contiguous(),
+                    g[:, :T1].contiguous(), beta[:, :T1].contiguous(), 1.0, st, final_state=st)
+    o2, _ = kda.fwd(q[:, T1:].contiguous(), k[:, T1:].contiguous(), v[:, T1:].contiguous(),
+                    g[:, T1:].contiguous(), beta[:, T1:].contiguous(), 1.0, st, final_state=st)
+    o_ref, S_ref = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta, 1.0, inp.S0)
+    o_split = torch.cat([o1, o2], dim=1)
+    assert err(host(o_split), o_ref, "bf16") <= tol("bf16")
+    assert err(host(st), S_ref, "bf16") <= tol("bf16")
+    assert err(host(o_full), host(o_split), "bf16") <= tol("bf16")
+
+
+def test_prefill_equals_decode_steps():
+    """The chunked prefill and T single-token decode steps agree (both against the oracle)."""
+    inp = ki.make_dense(1, 70, 2, 128, 128, "f32", 81, s0_std=0.2)
+    q, k, v, g, beta, S0, _ = upload(inp)
+    o_pf, S_pf = kda.fwd(q, k, v, g, beta, 1.0, S0)
+    st = S0.clone()
+    outs = [kda.decode_step(q[:, t].contiguous(), k[:, t].contiguous(), v[:, t].contiguous(),
+                            g[:, t].contiguous(), beta[:, t].contiguous(), st) for t in range(inp.T)]
+    o_dec = torch.stack(outs, dim=1)
+    assert err(host(o_pf), host(o_dec), "f32") <= tol("f32")
+    assert err(host(S_pf), host(st), "f32") <= tol("f32")
