@@ -151,6 +151,9 @@ __device__ __forceinline__ ChunkPos locate_chunk(long slot, const int32_t *cu, i
 template <bool BF16, int D> struct ChunkSmem {
     using TIO = typename std::conditional<BF16, uint16_t, float>::type;
     static constexpr int GS = D + 4, KS = D + 8, VS = kChunk + 8, AS = kChunk + 4;
+    static constexpr int CQ = D / 4;          // channel quads
+    static constexpr int RG = 256 / CQ;       // row groups in the load / cumulative-sum layout
+    static constexpr int RPG = kChunk / RG;   // rows per group
     union {
         float G[kChunk][GS];  // cumulative log2-decay, then
         float T[kChunk][AS];  // the UT transform Tm
@@ -158,15 +161,36 @@ template <bool BF16, int D> struct ChunkSmem {
     union {
         struct { TIO K[kChunk][KS]; TIO Q[kChunk][KS]; } in;
         struct { float Akk[kChunk][AS]; float Aqk[kChunk][AS]; } a;
+        TIO VT[D][VS];        // V transposed (VT[j][t]), written once Akk and Aqk are dead
     } kq;
-    TIO VT[D][VS];            // V transposed: VT[j][t]
+    float tot[RG][D];         // per row-group sums of the log-decay (cumulative-sum carries)
     float bridge[6][D];
     float beta[kChunk];
     int flag;
 };
 
+// Four consecutive io elements kept in their storage form (bf16 bits or fp32).
+template <typename TIO> struct Raw4;
+template <> struct Raw4<uint16_t> {
+    uint2 w;
+    static __device__ __forceinline__ Raw4 load(const uint16_t *p) { return Raw4{*reinterpret_cast<const uint2 *>(p)}; }
+    static __device__ __forceinline__ Raw4 zero() { return Raw4{make_uint2(0u, 0u)}; }
+    __device__ __forceinline__ void store(uint16_t *p) const { *reinterpret_cast<uint2 *>(p) = w; }
+    __device__ __forceinline__ uint16_t elem(int u) const {
+        const uint32_t x = (u < 2) ? w.x : w.y;
+        return (uint16_t)((u & 1) ? (x >> 16) : (x & 0xffffu));
+    }
+};
+template <> struct Raw4<float> {
+    f32x4 w;
+    static __device__ __forceinline__ Raw4 load(const float *p) { return Raw4{*reinterpret_cast<const f32x4 *>(p)}; }
+    static __device__ __forceinline__ Raw4 zero() { return Raw4{zero4()}; }
+    __device__ __forceinline__ void store(float *p) const { *reinterpret_cast<f32x4 *>(p) = w; }
+    __device__ __forceinline__ float elem(int u) const { return w[u]; }
+};
+
 template <bool BF16, int D>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ k,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ v,
@@ -190,38 +214,42 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     const long rowstride = (long)H * D;  // elements between consecutive tokens
     const long base_in = (pos.tok0 * H + h) * (long)D;
 
-    // ---------------- phase 1: loads (rows >= Cc are zero)
-    if (tid == 0) sm.flag = 0;
-    for (int e = tid; e < kChunk * (D / 4); e += 256) {
-        const int t = e / (D / 4), c4 = (e % (D / 4)) * 4;
-        f32x4 x = zero4();
-        if (t < Cc) x = *reinterpret_cast<const f32x4 *>(g + base_in + t * rowstride + c4);
-        *reinterpret_cast<f32x4 *>(&sm.g.G[t][c4]) = x * kLog2e;
-    }
-    for (int e = tid; e < kChunk * (D / 4); e += 256) {
-        const int t = e / (D / 4), c4 = (e % (D / 4)) * 4;
-        f32x4 kx = zero4(), qx = zero4(), vx = zero4();
-        if (t < Cc) {
-            kx = load4(k + base_in + t * rowstride + c4);
-            qx = load4(q + base_in + t * rowstride + c4);
-            vx = load4(v + base_in + t * rowstride + c4);
-        }
+    // ---------------- phase 1: loads (rows >= Cc are zero), cumulative log2-decay
+    // Thread (rg, cq) owns rows rg*RPG .. rg*RPG+RPG-1 and channels 4cq .. 4cq+3.  All global
+    // loads are issued before any of them is used.
+    using SM = ChunkSmem<BF16, D>;
+    constexpr int RPG = SM::RPG;
+    const int rg = tid / SM::CQ, c4 = (tid % SM::CQ) * 4;
+    f32x4 gv[RPG];
+    Raw4<TIO> kv[RPG], qv[RPG], vv[RPG];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            IO<TIO>::store(&sm.kq.in.K[t][0], c4 + u, kx[u]);
-            IO<TIO>::store(&sm.kq.in.Q[t][0], c4 + u, qx[u]);
-            IO<TIO>::store(&sm.VT[c4 + u][0], t, vx[u]);
-        }
+    for (int r = 0; r < RPG; ++r) {
+        const int t = rg * RPG + r;
+        const long off = base_in + t * rowstride + c4;
+        const bool in = t < Cc;
+        gv[r] = in ? *reinterpret_cast<const f32x4 *>(g + off) : zero4();
+        kv[r] = in ? Raw4<TIO>::load(k + off) : Raw4<TIO>::zero();
+        qv[r] = in ? Raw4<TIO>::load(q + off) : Raw4<TIO>::zero();
+        vv[r] = in ? Raw4<TIO>::load(v + off) : Raw4<TIO>::zero();
     }
-    if (tid < kChunk) sm.beta[tid] = tid < Cc ? beta[(pos.tok0 + tid) * H + h] : 0.f;
+    const float bt = (tid < Cc) ? beta[(pos.tok0 + tid) * H + h] : 0.f;
+    if (tid == 0) sm.flag = 0;
+    if (tid < kChunk) sm.beta[tid] = bt;
+    f32x4 run = zero4();
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        const int t = rg * RPG + r;
+        run += gv[r] * kLog2e;
+        gv[r] = run;
+        kv[r].store(&sm.kq.in.K[t][c4]);
+        qv[r].store(&sm.kq.in.Q[t][c4]);
+    }
+    *reinterpret_cast<f32x4 *>(&sm.tot[rg][c4]) = run;
     __syncthreads();
-    if (tid < D) {  // inclusive cumulative sum over the chunk, one channel per thread
-        float run = 0.f;
-        for (int t = 0; t < kChunk; ++t) {
-            run += sm.g.G[t][tid];
-            sm.g.G[t][tid] = run;
-        }
-    }
+    f32x4 carry = zero4();
+    for (int r2 = 0; r2 < rg; ++r2) carry += *reinterpret_cast<const f32x4 *>(&sm.tot[r2][c4]);
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) *reinterpret_cast<f32x4 *>(&sm.g.G[rg * RPG + r][c4]) = gv[r] + carry;
     __syncthreads();
 
     // ---------------- phase 2: element-wise products, written as operand fragments
@@ -415,7 +443,23 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
         __syncthreads();
     }
 
-    // ---------------- phase 5: W = T' X, U = T' V, Aqk fragments
+    // ---------------- phase 5: Aqk fragments; then V^T into the dead Akk/Aqk region;
+    // W = T' X and U = T' V.
+    for (int f = wave; f < 6; f += 4) {  // Aqk fragments
+        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
+        float vals[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) vals[s] = sm.kq.a.Aqk[16 * tt + r16][32 * kb2 + kslot(grp, s)];
+        P::st_split(wsA, L::nA, f, lane, P::split(vals));
+    }
+    __syncthreads();  // Akk, Aqk are dead from here on
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        const int t = rg * RPG + r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sm.kq.VT[c4 + u][t] = vv[r].elem(u);
+    }
+    __syncthreads();
     // T' = Tm Diag(beta) fragments; the same values serve as the A operand (row t, k = t')
     // of U and as the B operand (k = t', column t) of W^T.
     Split Tf[6];
@@ -448,7 +492,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             float vals[8];
 #pragma unroll
-            for (int s = 0; s < 8; ++s) vals[s] = IO<TIO>::load(&sm.VT[16 * jt + r16][0], 32 * kb2 + kslot(grp, s));
+            for (int s = 0; s < 8; ++s) vals[s] = IO<TIO>::load(&sm.kq.VT[16 * jt + r16][0], 32 * kb2 + kslot(grp, s));
             Vf[kb2] = P::plain(vals);
         }
 #pragma unroll
@@ -459,32 +503,44 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
             reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
         }
     }
-    for (int f = wave; f < 6; f += 4) {  // Aqk fragments
-        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
-        float vals[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) vals[s] = sm.kq.a.Aqk[16 * tt + r16][32 * kb2 + kslot(grp, s)];
-        P::st_split(wsA, L::nA, f, lane, P::split(vals));
-    }
 }
 
 // ------------------------------------------------------------------ kernel 2: state scan
-template <bool BF16, int D>
-__global__ void __launch_bounds__(64)
+// One workgroup = NWB waves = NWB tiles of 16 value columns of one (sequence, head) chain.
+// The operand fragments shared by all column tiles (W, Qh, Kh^T, Aqk: one contiguous block at
+// the start of the chunk's workspace record) are copied into LDS by direct global->LDS loads
+// one chunk ahead (double buffer when it fits), so the serial loop reads them from LDS; the
+// wave's own U tiles and e^gamma are prefetched into registers.
+template <bool BF16, int D> struct ScanStage {
+    using L = WsLayout<BF16, D>;
+    static constexpr size_t bytes = L::offU;                     // W, Qh, Kh^T, Aqk
+    static constexpr int kLoads = (int)(bytes / 1024);           // one 1 KB wave-load each
+    static constexpr bool kDouble = 2 * bytes <= 128 * 1024;
+    static constexpr int kBufs = kDouble ? 2 : 1;
+    static_assert(bytes % 1024 == 0, "staged block is a whole number of wave-loads");
+};
+
+template <bool BF16, int D, int NWB>
+__global__ void __launch_bounds__(64 * NWB)
 chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
                   const float *__restrict__ s0, float *__restrict__ sN,
                   typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     using P = Prec<BF16>;
     using L = WsLayout<BF16, D>;
+    using St = ScanStage<BF16, D>;
     using Split = typename P::Split;
-    constexpr int NKB = L::NKB, NRT = L::NRT, NJT = D / 16;
-    // the NJT column tiles of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
+    constexpr int NKB = L::NKB, NRT = L::NRT, NJT = D / 16, GPC = NJT / NWB;
+    static_assert(GPC * NWB == NJT, "column tiles per workgroup");
+    __shared__ __attribute__((aligned(16))) char stage[St::kBufs][St::bytes];
+
+    // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
     const int b = blockIdx.x, xcd = b & 7, sl = b >> 3;
-    const int jt = sl % NJT, chain = (sl / NJT) * 8 + xcd;
-    if (chain >= nchains) return;
+    const int jg = sl % GPC, chain = (sl / GPC) * 8 + xcd;
+    if (chain >= nchains) return;  // uniform over the workgroup
     const int n = chain / H, h = chain % H;
-    const int lane = threadIdx.x, grp = lane >> 4, r16 = lane & 15;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
+    const int jt = jg * NWB + wave;
     const int col = 16 * jt + r16;
 
     long s_tok, L_n, slot0;
@@ -498,6 +554,24 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         slot0 = (long)n * ((T + kChunk - 1) / kChunk);
     }
     const long nck = (L_n + kChunk - 1) / kChunk;
+    auto record = [&](long c) { return ws + ((size_t)(slot0 + c) * H + h) * L::bytes; };
+    auto stage_chunk = [&](long c, int buf) {
+        const char *src = record(c);
+        for (int i = wave; i < St::kLoads; i += NWB)
+            __builtin_amdgcn_global_load_lds(src + (size_t)i * 1024 + lane * 16,
+                                             (__attribute__((address_space(3))) void *)(&stage[buf][i * 1024]),
+                                             16, 0, 0);
+    };
+    f32x4 u_nx[4], e_nx[NRT];
+    auto prefetch_regs = [&](long c) {
+        const char *rec = record(c);
+        const f32x4 *pu = reinterpret_cast<const f32x4 *>(rec + L::offU);
+        const float *pe = reinterpret_cast<const float *>(rec + L::offE);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) u_nx[tt] = pu[(jt * 4 + tt) * 64 + lane];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) e_nx[rt] = *reinterpret_cast<const f32x4 *>(pe + 16 * rt + 4 * grp);
+    };
 
     f32x4 S[NRT];
     const long sbase = (long)chain * D * D;
@@ -506,8 +580,24 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
         for (int e = 0; e < 4; ++e) S[rt][e] = s0 ? s0[sbase + (long)(16 * rt + 4 * grp + e) * D + col] : 0.f;
 
+    if (nck > 0) {
+        stage_chunk(0, 0);
+        prefetch_regs(0);
+    }
     for (long c = 0; c < nck; ++c) {
-        const char *wsb = ws + ((size_t)(slot0 + c) * H + h) * L::bytes;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and stores) have landed
+        __syncthreads();                // ... and every other wave's: chunk c is in LDS
+        const int buf = St::kDouble ? (int)(c & 1) : 0;
+        f32x4 u_cur[4], e_cur[NRT];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) u_cur[tt] = u_nx[tt];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) e_cur[rt] = e_nx[rt];
+        if (St::kDouble && c + 1 < nck) {
+            stage_chunk(c + 1, buf ^ 1);
+            prefetch_regs(c + 1);
+        }
+        const char *sb = stage[buf];
         const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
         const long tok0 = s_tok + c * kChunk;
         Split Sop[NKB];
@@ -518,16 +608,15 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             Sop[kb] = P::split(vals);
         }
         f32x4 ud[4], oacc[4];
-        const f32x4 *wsU = reinterpret_cast<const f32x4 *>(wsb + L::offU);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             f32x4 ws_acc = zero4(), oa = zero4();
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                ws_acc = mfma(P::ld_plain(wsb + L::offW, L::nW, tt * NKB + kb, lane), Sop[kb], ws_acc);
-                oa = mfma(P::ld_plain(wsb + L::offQ, L::nQ, tt * NKB + kb, lane), Sop[kb], oa);
+                ws_acc = mfma(P::ld_plain(sb + L::offW, L::nW, tt * NKB + kb, lane), Sop[kb], ws_acc);
+                oa = mfma(P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + kb, lane), Sop[kb], oa);
             }
-            ud[tt] = wsU[(jt * 4 + tt) * 64 + lane] - ws_acc;
+            ud[tt] = u_cur[tt] - ws_acc;
             oacc[tt] = oa;
         }
         Split Uop[2];
@@ -538,25 +627,28 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             Uop[kb2] = P::split(vals);
         }
 #pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            f32x4 acc = S[rt] * e_cur[rt];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+                acc = mfma(P::ld_plain(sb + L::offK, L::nK, rt * 2 + kb2, lane), Uop[kb2], acc);
+            S[rt] = acc;
+        }
+#pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
 #pragma unroll
             for (int kb2 = 0; kb2 <= tt / 2; ++kb2)
-                oacc[tt] = mfma(P::ld_split(wsb + L::offA, L::nA, aidx(tt, kb2), lane), Uop[kb2], oacc[tt]);
+                oacc[tt] = mfma(P::ld_split(sb + L::offA, L::nA, aidx(tt, kb2), lane), Uop[kb2], oacc[tt]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 16 * tt + 4 * grp + e;
                 if (t < Cc) IO<TIO>::store(o, ((tok0 + t) * H + h) * (long)D + col, scale * oacc[tt][e]);
             }
         }
-        const float *wsE = reinterpret_cast<const float *>(wsb + L::offE);
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            const f32x4 eg = *reinterpret_cast<const f32x4 *>(wsE + 16 * rt + 4 * grp);
-            f32x4 acc = S[rt] * eg;
-#pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-                acc = mfma(P::ld_plain(wsb + L::offK, L::nK, rt * 2 + kb2, lane), Uop[kb2], acc);
-            S[rt] = acc;
+        if (!St::kDouble && c + 1 < nck) {
+            __syncthreads();  // every wave is done with the single buffer
+            stage_chunk(c + 1, 0);
+            prefetch_regs(c + 1);
         }
     }
     if (sN) {
@@ -589,15 +681,30 @@ static hipError_t launch_local_t(const FwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <bool BF16, int D, int NWB>
+static hipError_t launch_scan_nwb(const FwdArgs &a, hipStream_t st, int nchains) {
+    using TIO = typename ChunkSmem<BF16, D>::TIO;
+    const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NWB);
+    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NWB>), dim3((unsigned)blocks), dim3(64 * NWB), 0, st,
+                       a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale, a.s0, a.sN, (TIO *)a.o, (const char *)a.ws);
+    return hipGetLastError();
+}
+
+// Column tiles per workgroup: the largest of 4, 2, 1 that still gives every CU a workgroup
+// (more tiles per workgroup share one LDS copy of the chunk's operands).
 template <bool BF16, int D>
 static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
-    using TIO = typename ChunkSmem<BF16, D>::TIO;
     const int nchains = a.N * a.H;
     if (nchains <= 0) return hipSuccess;
-    const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16);
-    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D>), dim3((unsigned)blocks), dim3(64), 0, st, a.cu_seqlens, a.N,
-                       a.T, a.H, nchains, a.scale, a.s0, a.sN, (TIO *)a.o, (const char *)a.ws);
-    return hipGetLastError();
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    const long tiles = (long)nchains * (D / 16);
+    if (D / 16 >= 4 && tiles / 4 >= cus) return launch_scan_nwb<BF16, D, 4>(a, st, nchains);
+    if (tiles / 2 >= cus) return launch_scan_nwb<BF16, D, 2>(a, st, nchains);
+    return launch_scan_nwb<BF16, D, 1>(a, st, nchains);
 }
 
 hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {
