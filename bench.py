@@ -10,12 +10,16 @@ The same run also measures
   * the fp64 CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel times come from HIP events recorded on the stream the kernels run on.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-decode] [--no-prep]
-Prints one JSON line.
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,cpu,copy]
+Prints one JSON line.  `--only copy` runs a plain 256 MiB device copy (a kernel of known size
+used to calibrate the FETCH_SIZE / WRITE_SIZE counters of profiler runs).
+The roofline "traffic" figure comes from profiles/traffic.json (counter runs of this same
+script); it is reported only while the hash of the kernel source recorded there matches.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -167,17 +171,57 @@ def bench_prep(args, torch, kda, dev):
     return dict(ms=ms, tokens=ntok, bytes=nbytes, gbs=nbytes / ms / 1e6)
 
 
-def cpu_baseline(inp):
+def cpu_baseline(inp, min_seconds=10.0):
+    """The fp64 oracle on the prefill batch, repeated whole passes until ~10 s of wall time."""
     import oracle
     threads = oracle.default_threads()
     R = oracle.Recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+    passes = 0
     t0 = time.perf_counter()
-    R.run(threads=threads)
-    wall = time.perf_counter() - t0
-    tokens = inp.B * inp.T
+    while True:
+        R.run(threads=threads)
+        passes += 1
+        wall = time.perf_counter() - t0
+        if wall >= min_seconds or passes >= 200:
+            break
+    tokens = inp.B * inp.T * passes
     return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole prefill batch: all {inp.B * inp.H} (sequence, head) chains of "
-                      f"{inp.T} tokens, fp64 token recurrence, {wall:.2f} s wall"}
+            "sample": f"{passes} whole passes over the prefill batch (all {inp.B * inp.H} (sequence, head) "
+                      f"chains of {inp.T} tokens), fp64 token recurrence, {wall:.1f} s wall"}
+
+
+def bench_copy(torch, dev):
+    """256 MiB device-to-device copy: the reference kernel for counter calibration."""
+    x = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    x.fill_(1)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    ms = time_events(lambda: y.copy_(x), 5, torch)
+    return {"bytes_read": 1 << 28, "bytes_written": 1 << 28, "ms": ms, "GBs": 2 * (1 << 28) / ms / 1e6}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "gated_delta_rule_93_amd", "csrc"))):
+        with open(os.path.join(ROOT, "gated_delta_rule_93_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from profiles/traffic.json, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
 
 
 def main():
@@ -185,10 +229,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-prep", action="store_true")
+    ap.add_argument("--only", default="prefill,decode,prep,cpu",
+                    help="comma list of prefill, decode, prep, cpu, copy")
     args = ap.parse_args()
+    only = set(x.strip() for x in args.only.split(",") if x.strip())
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the operator shards by head and sequence with no exchange)", file=sys.stderr)
@@ -198,17 +242,37 @@ def main():
     dev = torch.device("cuda:0")
     kda.lib()
 
+    if "prefill" not in only:  # profiling-only invocations
+        out = {}
+        if "decode" in only:
+            out["decode"] = bench_decode(args, torch, kda, dev)
+        if "prep" in only:
+            out["prep"] = bench_prep(args, torch, kda, dev)
+        if "copy" in only:
+            out["copy"] = bench_copy(torch, dev)
+        print(json.dumps(out), flush=True)
+        return
     log("prefill ...")
     pf, inp = bench_prefill(args, torch, kda, dev)
     token_heads = pf["token_heads"]
     value = pf["tokens"] / (pf["ms_step"] / 1e3)
     # dominant prefill kernel and its roofline (HBM-bound by arithmetic intensity)
-    if pf["ms_chunk_local"] >= pf["ms_state_scan"]:
-        dom, dom_ms, dom_bytes = "chunk_local_kernel", pf["ms_chunk_local"], PREFILL_IN_BYTES * token_heads
-    else:
-        dom, dom_ms, dom_bytes = "chunk_scan_kernel", pf["ms_state_scan"], PREFILL_OUT_BYTES * token_heads
-    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
     flops = PREFILL_FLOP * token_heads
+    if pf["ms_chunk_local"] >= pf["ms_state_scan"]:
+        # chunk-local kernel: streams the inputs; HBM-bound by arithmetic intensity
+        dom, dom_ms = "chunk_local_kernel", pf["ms_chunk_local"]
+        roof = {"bound": "hbm", "kernel": dom, "algorithmic_bytes_per_launch": PREFILL_IN_BYTES * token_heads,
+                "achieved": PREFILL_IN_BYTES * token_heads / (dom_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        # state scan: its algorithmic work is the inter-chunk contractions (6 d^2 + (C+1) d per token-head)
+        dom, dom_ms = "chunk_scan_kernel", pf["ms_state_scan"]
+        scan_flop = (6 * 128 * 128 + 65 * 128) * token_heads
+        roof = {"bound": "mfma", "kernel": dom, "algorithmic_flop_per_launch": scan_flop,
+                "achieved": scan_flop / (dom_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(dom)
+    roof["ms_per_launch"] = dom_ms
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pf["ms_step"], "higher_is_better": True, "scaling": "weak",
@@ -216,9 +280,7 @@ def main():
         "config": {"workload": "KDA chunked prefill B=4 H=16 T=4096 d_k=d_v=128 chunk=64, bf16 q/k/v, "
                                "fp32 log-decay/beta/state", "global_batch": 4, "seq_len": 4096, "heads": 16,
                    "head_dim": 128, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "algorithmic_bytes_per_launch": dom_bytes, "ms_per_launch": dom_ms},
+        "roofline": roof,
         "prefill": {"ms_fwd": pf["ms_fwd_events"], "ms_chunk_local": pf["ms_chunk_local"],
                     "ms_state_scan": pf["ms_state_scan"],
                     "algorithmic_GBs": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * token_heads / pf["ms_fwd_events"] / 1e6,
@@ -226,20 +288,24 @@ def main():
                     "mfma_frac_of_bf16_peak": flops / pf["ms_fwd_events"] / 1e9 / BF16_PEAK_TFLOPS,
                     "workspace_bytes_per_chunk_head": pf["ws_bytes_per_chunk_head"]},
     }
-    if not args.no_decode:
+    if "decode" in only:
         log("decode ...")
         dc = bench_decode(args, torch, kda, dev)
         out["decode"] = {"workload": "256 sequences x 32 heads, d=128, fp32 state, bf16 tokens, 100 steps",
                          "ms_per_step": dc["ms_step"], "state_GBs": dc["state_gbs"], "total_GBs": dc["total_gbs"],
                          "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": dc["total_gbs"],
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": dc["total_gbs"] / HBM_PEAK_GBS, "traffic": None}}
-    if not args.no_prep:
+                                      "frac": dc["total_gbs"] / HBM_PEAK_GBS,
+                                      "traffic": measured_traffic("decode_step_kernel"),
+                                      "algorithmic_bytes_per_launch": dc["state_bytes"] + dc["io_bytes"]}}
+    if "prep" in only:
         log("prep ...")
         pr = bench_prep(args, torch, kda, dev)
         out["prep"] = {"workload": f"{pr['tokens']} packed tokens (64 sequences), H=32, d=128, width 4, bf16",
                        "ms": pr["ms"], "GBs": pr["gbs"], "frac": pr["gbs"] / HBM_PEAK_GBS}
-    if not args.no_cpu:
+    if "copy" in only:
+        out["copy"] = bench_copy(torch, dev)
+    if "cpu" in only:
         log("cpu baseline ...")
         out["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(out), flush=True)

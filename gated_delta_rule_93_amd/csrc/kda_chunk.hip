@@ -195,7 +195,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ k,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta,
-                   const int32_t *__restrict__ cu, int N, int T, int H, char *__restrict__ ws) {
+                   const int32_t *__restrict__ cu, int N, int T, int H, long nslots, char *__restrict__ ws) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     using P = Prec<BF16>;
     using L = WsLayout<BF16, D>;
@@ -204,8 +204,22 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     constexpr int NKB = L::NKB, NRT = L::NRT;
     __shared__ ChunkSmem<BF16, D> sm;
 
-    const long slot = blockIdx.x;
-    const int h = blockIdx.y;
+    // 1-D grid in reverse consumption order: the chunks the state scan reads first are written
+    // last, so they are the most likely to still be in the memory-side cache.
+    long slot;
+    int h;
+    const long id = blockIdx.x;
+    if (cu) {
+        slot = nslots - 1 - id / H;
+        h = (int)(id % H);
+    } else {
+        const int ncs = (T + kChunk - 1) / kChunk;
+        const long per_c = (long)N * H;
+        const int c = ncs - 1 - (int)(id / per_c);
+        const long rem = id % per_c;
+        h = (int)(rem % H);
+        slot = (rem / H) * ncs + c;
+    }
     const ChunkPos pos = locate_chunk(slot, cu, N, T);
     if (!pos.valid) return;  // uniform over the block
     const int Cc = pos.Cc;
@@ -506,11 +520,14 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 }
 
 // ------------------------------------------------------------------ kernel 2: state scan
-// One workgroup = NWB waves = NWB tiles of 16 value columns of one (sequence, head) chain.
-// The operand fragments shared by all column tiles (W, Qh, Kh^T, Aqk: one contiguous block at
-// the start of the chunk's workspace record) are copied into LDS by direct global->LDS loads
-// one chunk ahead (double buffer when it fits), so the serial loop reads them from LDS; the
-// wave's own U tiles and e^gamma are prefetched into registers.
+// A workgroup serves NCT tiles of 16 value columns of one (sequence, head) chain with two waves
+// per tile: wave `half` keeps rows half*D/2 .. of the tile's fp32 state in accumulator registers.
+// Per chunk each wave forms its half of W S and Qh S, the halves are summed through LDS (in
+// the same order by both waves, so both hold bit-identical Ud), and each wave then updates its
+// own state rows and writes two of the four 16-token output tiles.
+// The operand fragments shared by all tiles (W, Qh, Kh^T, Aqk: one contiguous block at the
+// start of the chunk's workspace record) are copied into LDS by direct global->LDS loads one
+// chunk ahead (double buffer when it fits); U and e^gamma go to registers one chunk ahead.
 template <bool BF16, int D> struct ScanStage {
     using L = WsLayout<BF16, D>;
     static constexpr size_t bytes = L::offU;                     // W, Qh, Kh^T, Aqk
@@ -520,8 +537,8 @@ template <bool BF16, int D> struct ScanStage {
     static_assert(bytes % 1024 == 0, "staged block is a whole number of wave-loads");
 };
 
-template <bool BF16, int D, int NWB>
-__global__ void __launch_bounds__(64 * NWB)
+template <bool BF16, int D, int NCT>
+__global__ void __launch_bounds__(128 * NCT)
 chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
                   const float *__restrict__ s0, float *__restrict__ sN,
                   typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws) {
@@ -530,9 +547,12 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     using L = WsLayout<BF16, D>;
     using St = ScanStage<BF16, D>;
     using Split = typename P::Split;
-    constexpr int NKB = L::NKB, NRT = L::NRT, NJT = D / 16, GPC = NJT / NWB;
-    static_assert(GPC * NWB == NJT, "column tiles per workgroup");
+    constexpr int NKB = L::NKB, NRT = L::NRT, NJT = D / 16, GPC = NJT / NCT;
+    constexpr int KBH = NKB / 2, RTH = NRT / 2;  // k-blocks and row tiles per half
+    constexpr int NW = 2 * NCT;
+    static_assert(GPC * NCT == NJT && KBH >= 1, "tiling");
     __shared__ __attribute__((aligned(16))) char stage[St::kBufs][St::bytes];
+    __shared__ f32x4 xch[NCT][2][2][4][64];  // [tile][half][W S | Qh S][token tile][lane]
 
     // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
     const int b = blockIdx.x, xcd = b & 7, sl = b >> 3;
@@ -540,8 +560,11 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     if (chain >= nchains) return;  // uniform over the workgroup
     const int n = chain / H, h = chain % H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
-    const int jt = jg * NWB + wave;
+    const int ct = wave >> 1, half = wave & 1;
+    const int jt = jg * NCT + ct;
     const int col = 16 * jt + r16;
+    // output token tiles of this wave: {0, 3} for half 0, {1, 2} for half 1 (equal MFMA work)
+    const int ot0 = half ? 1 : 0, ot1 = half ? 2 : 3;
 
     long s_tok, L_n, slot0;
     if (cu) {
@@ -554,15 +577,16 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         slot0 = (long)n * ((T + kChunk - 1) / kChunk);
     }
     const long nck = (L_n + kChunk - 1) / kChunk;
+    const int HD = H * D;
     auto record = [&](long c) { return ws + ((size_t)(slot0 + c) * H + h) * L::bytes; };
     auto stage_chunk = [&](long c, int buf) {
         const char *src = record(c);
-        for (int i = wave; i < St::kLoads; i += NWB)
+        for (int i = wave; i < St::kLoads; i += NW)
             __builtin_amdgcn_global_load_lds(src + (size_t)i * 1024 + lane * 16,
                                              (__attribute__((address_space(3))) void *)(&stage[buf][i * 1024]),
                                              16, 0, 0);
     };
-    f32x4 u_nx[4], e_nx[NRT];
+    f32x4 u_nx[4], e_nx[RTH];
     auto prefetch_regs = [&](long c) {
         const char *rec = record(c);
         const f32x4 *pu = reinterpret_cast<const f32x4 *>(rec + L::offU);
@@ -570,55 +594,77 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) u_nx[tt] = pu[(jt * 4 + tt) * 64 + lane];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) e_nx[rt] = *reinterpret_cast<const f32x4 *>(pe + 16 * rt + 4 * grp);
+        for (int r = 0; r < RTH; ++r)
+            e_nx[r] = *reinterpret_cast<const f32x4 *>(pe + 16 * (half * RTH + r) + 4 * grp);
+    };
+    // deferred output of the previous chunk (stored after the next chunk's copies are issued)
+    f32x4 o_pend[2];
+    long o_tok0 = 0;
+    int o_Cc = 0;
+    auto store_out = [&]() {
+        TIO *ob = o + (o_tok0 * H + h) * (long)D + col;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int tt = i ? ot1 : ot0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * tt + 4 * grp + e;
+                if (t < o_Cc) IO<TIO>::store(ob, (long)t * HD, scale * o_pend[i][e]);
+            }
+        }
     };
 
-    f32x4 S[NRT];
+    f32x4 S[RTH];
     const long sbase = (long)chain * D * D;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt)
+    for (int r = 0; r < RTH; ++r)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) S[rt][e] = s0 ? s0[sbase + (long)(16 * rt + 4 * grp + e) * D + col] : 0.f;
+        for (int e = 0; e < 4; ++e)
+            S[r][e] = s0 ? s0[sbase + (long)(16 * (half * RTH + r) + 4 * grp + e) * D + col] : 0.f;
 
     if (nck > 0) {
         stage_chunk(0, 0);
         prefetch_regs(0);
     }
     for (long c = 0; c < nck; ++c) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and stores) have landed
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
         __syncthreads();                // ... and every other wave's: chunk c is in LDS
         const int buf = St::kDouble ? (int)(c & 1) : 0;
-        f32x4 u_cur[4], e_cur[NRT];
+        f32x4 u_cur[4], e_cur[RTH];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) u_cur[tt] = u_nx[tt];
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) e_cur[rt] = e_nx[rt];
+        for (int r = 0; r < RTH; ++r) e_cur[r] = e_nx[r];
         if (St::kDouble && c + 1 < nck) {
             stage_chunk(c + 1, buf ^ 1);
             prefetch_regs(c + 1);
         }
+        if (c > 0) store_out();
         const char *sb = stage[buf];
-        const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
-        const long tok0 = s_tok + c * kChunk;
-        Split Sop[NKB];
+        // this half's contribution to W S and Qh S
+        Split Sop[KBH];
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            float vals[8] = {S[2 * kb][0], S[2 * kb][1], S[2 * kb][2], S[2 * kb][3],
-                             S[2 * kb + 1][0], S[2 * kb + 1][1], S[2 * kb + 1][2], S[2 * kb + 1][3]};
-            Sop[kb] = P::split(vals);
+        for (int kk = 0; kk < KBH; ++kk) {
+            float vals[8] = {S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3],
+                             S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
+            Sop[kk] = P::split(vals);
         }
-        f32x4 ud[4], oacc[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            f32x4 ws_acc = zero4(), oa = zero4();
+            f32x4 wsa = zero4(), qsa = zero4();
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                ws_acc = mfma(P::ld_plain(sb + L::offW, L::nW, tt * NKB + kb, lane), Sop[kb], ws_acc);
-                oa = mfma(P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + kb, lane), Sop[kb], oa);
+            for (int kk = 0; kk < KBH; ++kk) {
+                const int kb = half * KBH + kk;
+                wsa = mfma(P::ld_plain(sb + L::offW, L::nW, tt * NKB + kb, lane), Sop[kk], wsa);
+                qsa = mfma(P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + kb, lane), Sop[kk], qsa);
             }
-            ud[tt] = u_cur[tt] - ws_acc;
-            oacc[tt] = oa;
+            xch[ct][half][0][tt][lane] = wsa;
+            xch[ct][half][1][tt][lane] = qsa;
         }
+        __syncthreads();
+        f32x4 ud[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) ud[tt] = u_cur[tt] - (xch[ct][0][0][tt][lane] + xch[ct][1][0][tt][lane]);
         Split Uop[2];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -627,35 +673,37 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             Uop[kb2] = P::split(vals);
         }
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt) {
-            f32x4 acc = S[rt] * e_cur[rt];
+        for (int i = 0; i < 2; ++i) {
+            const int tt = i ? ot1 : ot0;
+            f32x4 oa = xch[ct][0][1][tt][lane] + xch[ct][1][1][tt][lane];
+            for (int kb2 = 0; kb2 <= tt / 2; ++kb2)
+                oa = mfma(P::ld_split(sb + L::offA, L::nA, aidx(tt, kb2), lane), Uop[kb2], oa);
+            o_pend[i] = oa;
+        }
+#pragma unroll
+        for (int r = 0; r < RTH; ++r) {
+            const int rt = half * RTH + r;
+            f32x4 acc = S[r] * e_cur[r];
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
                 acc = mfma(P::ld_plain(sb + L::offK, L::nK, rt * 2 + kb2, lane), Uop[kb2], acc);
-            S[rt] = acc;
+            S[r] = acc;
         }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-            for (int kb2 = 0; kb2 <= tt / 2; ++kb2)
-                oacc[tt] = mfma(P::ld_split(sb + L::offA, L::nA, aidx(tt, kb2), lane), Uop[kb2], oacc[tt]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tt + 4 * grp + e;
-                if (t < Cc) IO<TIO>::store(o, ((tok0 + t) * H + h) * (long)D + col, scale * oacc[tt][e]);
-            }
-        }
+        o_tok0 = s_tok + c * kChunk;
+        o_Cc = (int)min((long)kChunk, L_n - c * kChunk);
         if (!St::kDouble && c + 1 < nck) {
             __syncthreads();  // every wave is done with the single buffer
             stage_chunk(c + 1, 0);
             prefetch_regs(c + 1);
         }
     }
+    if (nck > 0) store_out();
     if (sN) {
 #pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
+        for (int r = 0; r < RTH; ++r)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sN[sbase + (long)(16 * rt + 4 * grp + e) * D + col] = S[rt][e];
+            for (int e = 0; e < 4; ++e)
+                sN[sbase + (long)(16 * (half * RTH + r) + 4 * grp + e) * D + col] = S[r][e];
     }
 }
 
@@ -675,23 +723,23 @@ static hipError_t launch_local_t(const FwdArgs &a, hipStream_t st) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     const long slots = fwd_chunk_slots(a.B, a.T, a.N, a.cu_seqlens != nullptr);
     if (slots <= 0 || a.H <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_local_kernel<BF16, D>), dim3((unsigned)slots, (unsigned)a.H), dim3(256), 0, st,
+    hipLaunchKernelGGL((chunk_local_kernel<BF16, D>), dim3((unsigned)(slots * a.H)), dim3(256), 0, st,
                        (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T,
-                       a.H, static_cast<char *>(a.ws));
+                       a.H, slots, static_cast<char *>(a.ws));
     return hipGetLastError();
 }
 
-template <bool BF16, int D, int NWB>
-static hipError_t launch_scan_nwb(const FwdArgs &a, hipStream_t st, int nchains) {
+template <bool BF16, int D, int NCT>
+static hipError_t launch_scan_nct(const FwdArgs &a, hipStream_t st, int nchains) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
-    const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NWB);
-    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NWB>), dim3((unsigned)blocks), dim3(64 * NWB), 0, st,
+    const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NCT);
+    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT>), dim3((unsigned)blocks), dim3(128 * NCT), 0, st,
                        a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale, a.s0, a.sN, (TIO *)a.o, (const char *)a.ws);
     return hipGetLastError();
 }
 
-// Column tiles per workgroup: the largest of 4, 2, 1 that still gives every CU a workgroup
-// (more tiles per workgroup share one LDS copy of the chunk's operands).
+// Column tiles per workgroup: two when that still gives every CU a workgroup (the tiles then
+// share one LDS copy of the chunk's operands), else one.
 template <bool BF16, int D>
 static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
     const int nchains = a.N * a.H;
@@ -702,9 +750,8 @@ static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
     const long tiles = (long)nchains * (D / 16);
-    if (D / 16 >= 4 && tiles / 4 >= cus) return launch_scan_nwb<BF16, D, 4>(a, st, nchains);
-    if (tiles / 2 >= cus) return launch_scan_nwb<BF16, D, 2>(a, st, nchains);
-    return launch_scan_nwb<BF16, D, 1>(a, st, nchains);
+    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2>(a, st, nchains);
+    return launch_scan_nct<BF16, D, 1>(a, st, nchains);
 }
 
 hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {

@@ -35,7 +35,9 @@ template <> struct IO<float> {
 };
 template <> struct IO<uint16_t> {
     static __device__ __forceinline__ float load(const uint16_t *p, long i) { return bf16_bits_to_f32(p[i]); }
-    static __device__ __forceinline__ void store(uint16_t *p, long i, float x) { p[i] = (uint16_t)f32_to_bf16_bits(x); }
+    static __device__ __forceinline__ void store(uint16_t *p, long i, float x) {
+        p[i] = __builtin_bit_cast(uint16_t, (__bf16)x);  // v_cvt_pk_bf16_f32: round to nearest even
+    }
 };
 
 // 4 consecutive elements as fp32 (p 8-byte aligned for bf16, 16-byte for fp32)
