@@ -236,17 +236,28 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     const int rg = tid / SM::CQ, c4 = (tid % SM::CQ) * 4;
     f32x4 gv[RPG];
     Raw4<TIO> kv[RPG], qv[RPG], vv[RPG];
+    // Rows past the end of a partial chunk read row 0 instead (always valid) and are zeroed
+    // afterwards, so every load is unconditional and all of them are in flight together.
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
         const int t = rg * RPG + r;
-        const long off = base_in + t * rowstride + c4;
-        const bool in = t < Cc;
-        gv[r] = in ? *reinterpret_cast<const f32x4 *>(g + off) : zero4();
-        kv[r] = in ? Raw4<TIO>::load(k + off) : Raw4<TIO>::zero();
-        qv[r] = in ? Raw4<TIO>::load(q + off) : Raw4<TIO>::zero();
-        vv[r] = in ? Raw4<TIO>::load(v + off) : Raw4<TIO>::zero();
+        const long off = base_in + (t < Cc ? t : 0) * rowstride + c4;
+        gv[r] = *reinterpret_cast<const f32x4 *>(g + off);
+        kv[r] = Raw4<TIO>::load(k + off);
+        qv[r] = Raw4<TIO>::load(q + off);
+        vv[r] = Raw4<TIO>::load(v + off);
     }
-    const float bt = (tid < Cc) ? beta[(pos.tok0 + tid) * H + h] : 0.f;
+    const float bt_raw = beta[(pos.tok0 + (tid < Cc ? tid : 0)) * H + h];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        if (rg * RPG + r >= Cc) {
+            gv[r] = zero4();
+            kv[r] = Raw4<TIO>::zero();
+            qv[r] = Raw4<TIO>::zero();
+            vv[r] = Raw4<TIO>::zero();
+        }
+    }
+    const float bt = tid < Cc ? bt_raw : 0.f;
     if (tid == 0) sm.flag = 0;
     if (tid < kChunk) sm.beta[tid] = bt;
     f32x4 run = zero4();
@@ -317,38 +328,48 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     if (span_bad) atomicOr(&sm.flag, 1);
     __syncthreads();
 
-    // ---------------- phase 3: decayed Gram matrices Akk, Aqk
+    // ---------------- phase 3: decayed Gram matrices Akk (times beta, strictly lower), Aqk
+    // Waves form two pair groups x two channel halves: wave (pg, ch) sums channels of half ch
+    // for the five sub-block pairs of group pg; one reduction round adds the two halves.
     const bool fallback = sm.flag != 0;
     if (!fallback) {
-        f32x4 accK[10], accQ[10];
+        constexpr int KBW = NKB / 2;  // channel k-blocks per half
+        const int pg = wave >> 1, ch = wave & 1;
+        f32x4 accK[5], accQ[5];
 #pragma unroll
-        for (int p = 0; p < 10; ++p) { accK[p] = zero4(); accQ[p] = zero4(); }
-        const bool has_work = wave < NKB;
-        if (has_work) {
-            for (int kb = wave; kb < NKB; kb += 4) {
+        for (int u = 0; u < 5; ++u) { accK[u] = zero4(); accQ[u] = zero4(); }
+        // the pair group is a compile-time constant inside, so every array index is static
+        auto gram_group = [&](auto pg_c) {
+            constexpr int PG = decltype(pg_c)::value;
+#pragma unroll
+            for (int kk = 0; kk < KBW; ++kk) {
+                const int kb = ch * KBW + kk;
+                // row factors of the blocks this group uses: pairs (0,0) (1,0) (1,1) (2,0) (2,1) for
+                // group 0, (2,2) (3,0) (3,1) (3,2) (3,3) for group 1
                 float kA[4][8], qA[4][8], kB[4][8];
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
+                    const bool needA = PG == 0 ? I <= 2 : I >= 2;
+                    const bool needB = PG == 0 ? I <= 1 : true;
+                    if (!needA && !needB) continue;
                     const int i = 16 * I + r16, m = mid_row(I);
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
                         const int c = 32 * kb + kslot(grp, s);
                         const float d = sm.g.G[i][c] - sm.g.G[m][c];
                         const float kv = IO<TIO>::load(&sm.kq.in.K[i][0], c);
-                        const float qv = IO<TIO>::load(&sm.kq.in.Q[i][0], c);
-                        const float fa = fast_exp2(d), fb = fast_exp2(-d);
-                        kA[I][s] = kv * fa;
-                        qA[I][s] = qv * fa;
-                        kB[I][s] = kv * fb;
+                        if (needA) {
+                            const float fa = fast_exp2(d);
+                            kA[I][s] = kv * fa;
+                            qA[I][s] = IO<TIO>::load(&sm.kq.in.Q[i][0], c) * fa;
+                        }
+                        if (needB) kB[I][s] = kv * fast_exp2(-d);
                     }
                 }
-                Split Bop[4];
 #pragma unroll
-                for (int J = 0; J < 4; ++J) Bop[J] = P::split(kB[J]);
-#pragma unroll
-                for (int p = 0; p < 10; ++p) {
+                for (int u = 0; u < 5; ++u) {
                     int I, J;
-                    pair_ij(p, I, J);
+                    pair_ij(PG * 5 + u, I, J);
                     float ak[8], aq[8];
 #pragma unroll
                     for (int s = 0; s < 8; ++s) {
@@ -357,34 +378,44 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                         ak[s] = kA[I][s] * br;
                         aq[s] = qA[I][s] * br;
                     }
-                    accK[p] = mfma(P::split(ak), Bop[J], accK[p]);
-                    accQ[p] = mfma(P::split(aq), Bop[J], accQ[p]);
+                    const Split bop = P::split(kB[J]);
+                    accK[u] = mfma(P::split(ak), bop, accK[u]);
+                    accQ[u] = mfma(P::split(aq), bop, accQ[u]);
                 }
             }
-        }
+        };
+        if (pg == 0) gram_group(std::integral_constant<int, 0>{});
+        else gram_group(std::integral_constant<int, 1>{});
         __syncthreads();  // every wave is done reading K, Q (aliased by Akk, Aqk below)
-        const int nw = NKB < 4 ? NKB : 4;
-        for (int r = 0; r < nw; ++r) {
-            if (wave == r) {
+        if (ch == 1) {
 #pragma unroll
-                for (int p = 0; p < 10; ++p) {
-                    int I, J;
-                    pair_ij(p, I, J);
+            for (int u = 0; u < 5; ++u) {
+                int I, J;
+                pair_ij(pg * 5 + u, I, J);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int row = 16 * I + 4 * grp + e, col = 16 * J + r16;
-                        if (r == 0) {
-                            sm.kq.a.Akk[row][col] = accK[p][e];
-                            sm.kq.a.Aqk[row][col] = accQ[p][e];
-                        } else {
-                            sm.kq.a.Akk[row][col] += accK[p][e];
-                            sm.kq.a.Aqk[row][col] += accQ[p][e];
-                        }
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * I + 4 * grp + e, col = 16 * J + r16;
+                    sm.kq.a.Akk[row][col] = accK[u][e];
+                    sm.kq.a.Aqk[row][col] = accQ[u][e];
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();
+        if (ch == 0) {
+#pragma unroll
+            for (int u = 0; u < 5; ++u) {
+                int I, J;
+                pair_ij(pg * 5 + u, I, J);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * I + 4 * grp + e, col = 16 * J + r16;
+                    // only the entries below the diagonal are ever read; beta scales Akk rows
+                    sm.kq.a.Akk[row][col] = (accK[u][e] + sm.kq.a.Akk[row][col]) * sm.beta[row];
+                    sm.kq.a.Aqk[row][col] = accQ[u][e] + sm.kq.a.Aqk[row][col];
+                }
+            }
+        }
+        __syncthreads();
     } else {
         // exact element-wise fallback for extreme decay inside a 16-token sub-block
         float rk[16], rq[16];
@@ -401,7 +432,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                     aq += IO<TIO>::load(&sm.kq.in.Q[i][0], c) * kj * e;
                 }
             }
-            rk[jj] = ak;
+            rk[jj] = ak * sm.beta[i];
             rq[jj] = aq;
         }
         __syncthreads();
@@ -412,15 +443,6 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
         }
         __syncthreads();
     }
-    // beta rows and the causal masks (also clears never-written upper blocks)
-    for (int e = tid; e < kChunk * kChunk; e += 256) {
-        const int i = e >> 6, j = e & 63;
-        const float a = sm.kq.a.Akk[i][j], b = sm.kq.a.Aqk[i][j];
-        sm.kq.a.Akk[i][j] = j < i ? sm.beta[i] * a : 0.f;
-        sm.kq.a.Aqk[i][j] = j <= i ? b : 0.f;
-        sm.g.T[i][j] = (j >> 4) > (i >> 4) ? 0.f : sm.g.T[i][j];
-    }
-    __syncthreads();
 
     // ---------------- phase 4: Tm = (I + Akk)^-1 (unit lower triangular), fp32
     if (wave == 0) {  // 16x16 diagonal blocks: lane owns column j of block b
@@ -463,7 +485,10 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
         const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
         float vals[8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) vals[s] = sm.kq.a.Aqk[16 * tt + r16][32 * kb2 + kslot(grp, s)];
+        for (int s = 0; s < 8; ++s) {
+            const int t = 16 * tt + r16, tp = 32 * kb2 + kslot(grp, s);
+            vals[s] = tp <= t ? sm.kq.a.Aqk[t][tp] : 0.f;  // causal mask, incl. the diagonal
+        }
         P::st_split(wsA, L::nA, f, lane, P::split(vals));
     }
     __syncthreads();  // Akk, Aqk are dead from here on
@@ -484,7 +509,8 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const int tp = 32 * kb2 + kslot(grp, s);
-            vals[s] = sm.g.T[16 * tt + r16][tp] * sm.beta[tp];
+            // Tm is zero above its 16x16 diagonal blocks (those entries are never written)
+            vals[s] = (tp >> 4) <= tt ? sm.g.T[16 * tt + r16][tp] * sm.beta[tp] : 0.f;
         }
         Tf[f] = P::split(vals);
     }
