@@ -60,15 +60,55 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
     return 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
 
 
-def _unit_rows(x: np.ndarray, block: int = 1 << 20) -> np.ndarray:
+def _blocks(n: int, block: int):
+    return [(s, min(s + block, n)) for s in range(0, n, block)]
+
+
+def _parallel(fn, n: int, block: int):
+    """Run fn(s, e) over row blocks [s, e) on a few threads (numpy ufuncs release the GIL).
+    Every block is an independent elementwise or per-row computation, so the result does
+    not depend on the blocking."""
+    bl = _blocks(n, block)
+    if len(bl) <= 1:
+        for s, e in bl:
+            fn(s, e)
+        return
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=min(8, len(bl))) as ex:
+        list(ex.map(lambda se: fn(*se), bl))
+
+
+def _unit_rows(x: np.ndarray, block: int = 1 << 18) -> np.ndarray:
     """Divide each last-axis row by its L2 norm (fp64 norm), returned as fp32."""
     flat = x.reshape(-1, x.shape[-1])
     out = np.empty(flat.shape, dtype=np.float32)
-    for s in range(0, flat.shape[0], block):
-        blk = flat[s:s + block].astype(np.float64)
-        nrm = np.sqrt(np.sum(blk * blk, axis=-1, keepdims=True))
-        out[s:s + block] = (blk / np.maximum(nrm, 1e-300)).astype(np.float32)
+
+    def blk(s, e):
+        b = flat[s:e].astype(np.float64)
+        nrm = np.sqrt(np.sum(b * b, axis=-1, keepdims=True))
+        out[s:e] = (b / np.maximum(nrm, 1e-300)).astype(np.float32)
+    _parallel(blk, flat.shape[0], block)
     return out.reshape(x.shape)
+
+
+def _map_f32(fn, x: np.ndarray, block: int = 1 << 24) -> np.ndarray:
+    """fp32 array of fn(x) (fn evaluated in fp64), computed over flat blocks."""
+    flat = x.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.float32)
+
+    def blk(s, e):
+        out[s:e] = fn(flat[s:e]).astype(np.float32)
+    _parallel(blk, flat.shape[0], block)
+    return out.reshape(x.shape)
+
+
+def _store_bf16_inplace(x: np.ndarray, block: int = 1 << 24) -> np.ndarray:
+    flat = x.reshape(-1)
+
+    def blk(s, e):
+        flat[s:e] = bf16_round(flat[s:e])
+    _parallel(blk, flat.shape[0], block)
+    return x
 
 
 # --------------------------------------------------------------------------- containers
@@ -122,9 +162,11 @@ def draw_tokens(rng: np.random.Generator, shape_tok, H: int, dk: int, dv: int, i
     if normalize_qk:
         q = _unit_rows(q)
         k = _unit_rows(k)
-    beta = _sigmoid(xb).astype(np.float32)
-    g = (-_softplus(xa.astype(np.float64) + g_shift)).astype(np.float32)
-    return _store(q, io), _store(k, io), _store(v, io), beta, g
+    beta = _map_f32(_sigmoid, xb)
+    g = _map_f32(lambda a: -_softplus(a.astype(np.float64) + g_shift), xa)
+    if io == "bf16":
+        q, k, v = (_store_bf16_inplace(a) for a in (q, k, v))
+    return q, k, v, beta, g
 
 
 def make_dense(B: int, T: int, H: int, dk: int, dv: int, io: str, seed: int,
@@ -215,3 +257,22 @@ CONFIG4 = dict(n_seq=64, lo=512, hi=16384, H=32, d=128, seed=SEED_BASE + 4)
 
 def config4_lengths() -> np.ndarray:
     return varlen_lengths(CONFIG4["n_seq"], CONFIG4["lo"], CONFIG4["hi"], CONFIG4["seed"])
+
+
+def config4_sequence(n: int, H: int = 32, d: int = 128, g_shift: float = 2.0):
+    """Sequence n of the varlen layer workload: raw q, k ~ N(0,1) (bf16, before the prologue),
+    v ~ N(0,1) bf16, beta, g, and S_0 ~ N(0, 0.02), all from default_rng([seed, n])."""
+    L = int(config4_lengths()[n])
+    rng = np.random.default_rng([CONFIG4["seed"], n])
+    q, k, v, beta, g = draw_tokens(rng, (L,), H, d, d, "bf16", g_shift, normalize_qk=False)
+    S0 = rng.standard_normal((H, d, d), dtype=np.float32) * np.float32(0.02)
+    return q, k, v, beta, g, S0
+
+
+def config4_conv_weights(H: int = 32, d: int = 128, width: int = 4):
+    """w_q, w_k [H*d, width] ~ N(0, 0.5), drawn after the lengths from the workload seed."""
+    rng = np.random.default_rng(CONFIG4["seed"])
+    rng.integers(CONFIG4["lo"], CONFIG4["hi"], size=CONFIG4["n_seq"], endpoint=True)
+    wq = rng.standard_normal((H * d, width), dtype=np.float32) * np.float32(0.5)
+    wk = rng.standard_normal((H * d, width), dtype=np.float32) * np.float32(0.5)
+    return wq, wk
