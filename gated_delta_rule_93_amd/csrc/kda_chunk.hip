@@ -86,7 +86,8 @@ template <> struct Prec<false> {
 
 // ------------------------------------------------------------------ workspace layout
 // Per (chunk slot, head): W, Qh fragments [tt][kb]; Kh^T fragments [rt][kb2]; Aqk fragments
-// (6 lower ones); U as accumulator tiles [jt][tt][lane] f32x4; e^gamma [D].
+// (6 lower ones); e^gamma [D] (padded to 1 KB); U as accumulator tiles [jt][tt][lane] f32x4.
+// Everything before U is read by every column tile of the chain; U tile jt by one.
 template <bool BF16, int D> struct WsLayout {
     static constexpr int NT = 4;           // 16-token tiles per chunk
     static constexpr int NKB = D / 32;     // 32-channel k-blocks
@@ -97,9 +98,10 @@ template <bool BF16, int D> struct WsLayout {
     static constexpr size_t offQ = offW + (size_t)nW * PP * 1024;
     static constexpr size_t offK = offQ + (size_t)nQ * PP * 1024;
     static constexpr size_t offA = offK + (size_t)nK * PP * 1024;
-    static constexpr size_t offU = offA + (size_t)nA * SP * 1024;
-    static constexpr size_t offE = offU + (size_t)NRT * NT * 1024;
-    static constexpr size_t bytes = (offE + (size_t)D * 4 + 255) / 256 * 256;
+    static constexpr size_t offE = offA + (size_t)nA * SP * 1024;
+    static constexpr size_t offU = offE + 1024;
+    static constexpr size_t bytes = offU + (size_t)NRT * NT * 1024;
+    static_assert(D * 4 <= 1024, "e^gamma fits its 1 KB slot");
 };
 
 // lower Aqk fragment index of (token tile tt, token k-block kb2), kb2 <= tt / 2
@@ -548,23 +550,30 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 // ------------------------------------------------------------------ kernel 2: state scan
 // A workgroup serves NCT tiles of 16 value columns of one (sequence, head) chain with two waves
 // per tile: wave `half` keeps rows half*D/2 .. of the tile's fp32 state in accumulator registers.
-// Per chunk each wave forms its half of W S and Qh S, the halves are summed through LDS (in
-// the same order by both waves, so both hold bit-identical Ud), and each wave then updates its
-// own state rows and writes two of the four 16-token output tiles.
-// The operand fragments shared by all tiles (W, Qh, Kh^T, Aqk: one contiguous block at the
-// start of the chunk's workspace record) are copied into LDS by direct global->LDS loads one
-// chunk ahead (double buffer when it fits); U and e^gamma go to registers one chunk ahead.
+// Per chunk each wave forms its half of W S and Qh S and hands the other wave, through LDS, the
+// partial sums that wave needs; both add the halves as (half 0) + (half 1), so both hold
+// bit-identical Ud.  Each wave then updates its own state rows and forms two of the four
+// 16-token output tiles.
+// The operands shared by all tiles (W, Qh, Kh^T, Aqk, e^gamma: one contiguous block at the start
+// of the chunk's workspace record) are copied into LDS by direct global->LDS loads.  When two
+// copies fit in LDS, one extra wave per workgroup (the producer) copies chunk c+1 while the
+// compute waves work on chunk c, and also writes the output rows, which the compute waves leave
+// in LDS: a wave stalls while the memory pipeline accepts its loads, and this keeps those
+// stalls off the waves that issue the MFMAs.  Otherwise the compute waves copy the next chunk
+// themselves after the current one.  U goes to registers one chunk ahead.
 template <bool BF16, int D> struct ScanStage {
     using L = WsLayout<BF16, D>;
-    static constexpr size_t bytes = L::offU;                     // W, Qh, Kh^T, Aqk
+    static constexpr size_t bytes = L::offU;                     // W, Qh, Kh^T, Aqk, e^gamma
     static constexpr int kLoads = (int)(bytes / 1024);           // one 1 KB wave-load each
-    static constexpr bool kDouble = 2 * bytes <= 128 * 1024;
-    static constexpr int kBufs = kDouble ? 2 : 1;
+    static constexpr bool kProducer = 2 * bytes <= 128 * 1024;   // double buffer + producer wave
     static_assert(bytes % 1024 == 0, "staged block is a whole number of wave-loads");
 };
 
 template <bool BF16, int D, int NCT>
-__global__ void __launch_bounds__(128 * NCT)
+constexpr int scan_threads() { return 64 * (2 * NCT + (ScanStage<BF16, D>::kProducer ? 1 : 0)); }
+
+template <bool BF16, int D, int NCT>
+__global__ void __launch_bounds__((scan_threads<BF16, D, NCT>()))
 chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
                   const float *__restrict__ s0, float *__restrict__ sN,
                   typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws) {
@@ -572,13 +581,23 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     using P = Prec<BF16>;
     using L = WsLayout<BF16, D>;
     using St = ScanStage<BF16, D>;
+    using Plain = typename P::Plain;
     using Split = typename P::Split;
+    constexpr bool kProd = St::kProducer;
     constexpr int NKB = L::NKB, NRT = L::NRT, NJT = D / 16, GPC = NJT / NCT;
     constexpr int KBH = NKB / 2, RTH = NRT / 2;  // k-blocks and row tiles per half
-    constexpr int NW = 2 * NCT;
+    constexpr int NW = 2 * NCT;                  // compute waves
+    constexpr int LPW = (St::kLoads + NW - 1) / NW;  // copies per compute wave (no producer)
+    constexpr int kCopyA = (St::kLoads + 1) / 2;     // producer copies issued before the exchange
+    constexpr int OC = NCT * 16;                     // output columns of the workgroup
     static_assert(GPC * NCT == NJT && KBH >= 1, "tiling");
-    __shared__ __attribute__((aligned(16))) char stage[St::kBufs][St::bytes];
-    __shared__ f32x4 xch[NCT][2][2][4][64];  // [tile][half][W S | Qh S][token tile][lane]
+    // two separate arrays (not one [2][bytes] array) so that alias analysis can tell a read of
+    // one buffer from an in-flight copy into the other
+    __shared__ __attribute__((aligned(16))) char stage0[St::bytes];
+    __shared__ __attribute__((aligned(16))) char stage1[kProd ? St::bytes : 16];
+    __shared__ f32x4 xws[NCT][2][4][64];  // [tile][from half][token tile][lane]: W S partials
+    __shared__ f32x4 xqs[NCT][2][2][64];  // Qh S partials of the receiving half's output tiles
+    __shared__ __attribute__((aligned(16))) TIO obuf[kProd ? kChunk : 1][kProd ? OC : 1];  // output rows
 
     // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
     const int b = blockIdx.x, xcd = b & 7, sl = b >> 3;
@@ -586,7 +605,8 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     if (chain >= nchains) return;  // uniform over the workgroup
     const int n = chain / H, h = chain % H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
-    const int ct = wave >> 1, half = wave & 1;
+    const bool producer = kProd && wave == NW;
+    const int ct = producer ? 0 : wave >> 1, half = wave & 1;
     const int jt = jg * NCT + ct;
     const int col = 16 * jt + r16;
     // output token tiles of this wave: {0, 3} for half 0, {1, 2} for half 1 (equal MFMA work)
@@ -604,40 +624,77 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     }
     const long nck = (L_n + kChunk - 1) / kChunk;
     const int HD = H * D;
-    auto record = [&](long c) { return ws + ((size_t)(slot0 + c) * H + h) * L::bytes; };
-    auto stage_chunk = [&](long c, int buf) {
-        const char *src = record(c);
-        for (int i = wave; i < St::kLoads; i += NW)
-            __builtin_amdgcn_global_load_lds(src + (size_t)i * 1024 + lane * 16,
-                                             (__attribute__((address_space(3))) void *)(&stage[buf][i * 1024]),
-                                             16, 0, 0);
+    auto record = [&](long c) __attribute__((always_inline)) { return ws + ((size_t)(slot0 + c) * H + h) * L::bytes; };
+    auto copy_one = [&](const char *src, char *dst, int i) __attribute__((always_inline)) {
+        __builtin_amdgcn_global_load_lds(src + (size_t)i * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0, 0);
     };
-    f32x4 u_nx[4], e_nx[RTH];
-    auto prefetch_regs = [&](long c) {
-        const char *rec = record(c);
-        const f32x4 *pu = reinterpret_cast<const f32x4 *>(rec + L::offU);
-        const float *pe = reinterpret_cast<const float *>(rec + L::offE);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+
+    // ================================================================ producer wave
+    if (producer) {
+        // wave-loads I0 <= i < I1 of chunk c into buffer BUF
+        auto copy_part = [&](long c, auto bufc, auto i0c, auto i1c) __attribute__((always_inline)) {
+            char *dst = decltype(bufc)::value ? stage1 : stage0;
+            const char *src = record(c);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) u_nx[tt] = pu[(jt * 4 + tt) * 64 + lane];
+            for (int i = decltype(i0c)::value; i < decltype(i1c)::value; ++i) copy_one(src, dst, i);
+        };
+        // output rows of chunk c: 16 bytes per lane, RPI token rows per instruction
+        auto store_rows = [&](long c) __attribute__((always_inline)) {
+            constexpr int LPR = OC * (int)sizeof(TIO) / 16, RPI = 64 / LPR, EPL = 16 / (int)sizeof(TIO);
+            static_assert(LPR * RPI == 64, "row split");
+            const long tok0 = s_tok + c * kChunk;
+            const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
+            const int r0 = lane / LPR, part = lane % LPR;
+            TIO *dst = o + (tok0 * H + h) * (long)D + jg * OC + part * EPL;
 #pragma unroll
-        for (int r = 0; r < RTH; ++r)
-            e_nx[r] = *reinterpret_cast<const f32x4 *>(pe + 16 * (half * RTH + r) + 4 * grp);
-    };
-    // deferred output of the previous chunk (stored after the next chunk's copies are issued)
-    f32x4 o_pend[2];
-    long o_tok0 = 0;
-    int o_Cc = 0;
-    auto store_out = [&]() {
-        TIO *ob = o + (o_tok0 * H + h) * (long)D + col;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tt = i ? ot1 : ot0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = 16 * tt + 4 * grp + e;
-                if (t < o_Cc) IO<TIO>::store(ob, (long)t * HD, scale * o_pend[i][e]);
+            for (int k = 0; k < kChunk / RPI; ++k) {
+                const int t = k * RPI + r0;
+                const uint4 val = *reinterpret_cast<const uint4 *>(&obuf[t][part * EPL]);
+                if (t < Cc) *reinterpret_cast<uint4 *>(dst + (long)t * HD) = val;
             }
+        };
+        using KA = std::integral_constant<int, kCopyA>;
+        using KL = std::integral_constant<int, St::kLoads>;
+        if (nck > 0) copy_part(0, I0{}, I0{}, KL{});
+        auto pstep = [&](long c, auto bufc) __attribute__((always_inline)) {
+            using NB = std::integral_constant<int, decltype(bufc)::value ^ 1>;
+            __builtin_amdgcn_s_waitcnt(0);  // copies of chunk c have landed
+            __syncthreads();
+            const bool more = c + 1 < nck;
+            if (c > 0) store_rows(c - 1);   // rows left in obuf before this barrier
+            if (more) copy_part(c + 1, NB{}, I0{}, KA{});
+            // exchange barrier (obuf has been read: the compute waves refill it after this)
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (more) copy_part(c + 1, NB{}, KA{}, KL{});
+        };
+        for (long c = 0; c < nck; c += 2) {
+            pstep(c, I0{});
+            if (c + 1 < nck) pstep(c + 1, I1{});
         }
+        __syncthreads();  // the last chunk's rows are in obuf
+        if (nck > 0) store_rows(nck - 1);
+        return;
+    }
+
+    // ================================================================ compute waves
+    // this wave's share of the copies of chunk c (no producer wave): wave-load j * NW + wave
+    auto stage_all = [&](long c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int i = j * NW + wave;
+            if (i < St::kLoads) copy_one(record(c), stage0, i);
+        }
+    };
+    // U tiles alternate between two register sets (even chunks in uA, odd in uB), so a
+    // prefetched tile is never copied between registers before it has arrived
+    f32x4 uA[4], uB[4];
+    auto prefetch_u = [&](long c, f32x4 (&u)[4]) __attribute__((always_inline)) {
+        const f32x4 *pu = reinterpret_cast<const f32x4 *>(record(c) + L::offU) + jt * 4 * 64 + lane;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) u[tt] = pu[tt * 64];
     };
 
     f32x4 S[RTH];
@@ -649,24 +706,33 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             S[r][e] = s0 ? s0[sbase + (long)(16 * (half * RTH + r) + 4 * grp + e) * D + col] : 0.f;
 
     if (nck > 0) {
-        stage_chunk(0, 0);
-        prefetch_regs(0);
+        if (!kProd) stage_all(0);
+        prefetch_u(0, uA);
     }
-    for (long c = 0; c < nck; ++c) {
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies have landed
-        __syncthreads();                // ... and every other wave's: chunk c is in LDS
-        const int buf = St::kDouble ? (int)(c & 1) : 0;
-        f32x4 u_cur[4], e_cur[RTH];
+    // One chunk.  The buffer index is a compile-time constant (the loop below is unrolled by
+    // two), so the compiler can tell the LDS reads of this chunk from the copies into the
+    // other buffer and does not make the reads wait for those copies.
+    auto chunk_step = [&](long c, auto bufc, f32x4 (&u_cur)[4], f32x4 (&u_nx)[4]) __attribute__((always_inline)) {
+        constexpr int buf = decltype(bufc)::value;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
+        __syncthreads();                // ... and every copy: chunk c is in LDS
+        const bool more = c + 1 < nck;
+        const char *sb = buf ? stage1 : stage0;
+        // W and Qh fragments of this half; bf16 ones are all requested before the first product
+        // (fp32 ones take twice the registers and are read next to their use)
+        auto ldW = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offW, L::nW, tt * NKB + half * KBH + kk, lane); };
+        auto ldQ = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + half * KBH + kk, lane); };
+        Plain wf[4][KBH], qf[4][KBH];
+        if (BF16) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) u_cur[tt] = u_nx[tt];
+            for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int r = 0; r < RTH; ++r) e_cur[r] = e_nx[r];
-        if (St::kDouble && c + 1 < nck) {
-            stage_chunk(c + 1, buf ^ 1);
-            prefetch_regs(c + 1);
+                for (int kk = 0; kk < KBH; ++kk) {
+                    wf[tt][kk] = ldW(tt, kk);
+                    qf[tt][kk] = ldQ(tt, kk);
+                }
         }
-        if (c > 0) store_out();
-        const char *sb = stage[buf];
+        if (more) prefetch_u(c + 1, u_nx);
         // this half's contribution to W S and Qh S
         Split Sop[KBH];
 #pragma unroll
@@ -675,22 +741,48 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
                              S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
             Sop[kk] = P::split(vals);
         }
+        f32x4 wsa[4], qsa[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            f32x4 wsa = zero4(), qsa = zero4();
+            wsa[tt] = zero4();
+            qsa[tt] = zero4();
 #pragma unroll
             for (int kk = 0; kk < KBH; ++kk) {
-                const int kb = half * KBH + kk;
-                wsa = mfma(P::ld_plain(sb + L::offW, L::nW, tt * NKB + kb, lane), Sop[kk], wsa);
-                qsa = mfma(P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + kb, lane), Sop[kk], qsa);
+                wsa[tt] = mfma(BF16 ? wf[tt][kk] : ldW(tt, kk), Sop[kk], wsa[tt]);
+                qsa[tt] = mfma(BF16 ? qf[tt][kk] : ldQ(tt, kk), Sop[kk], qsa[tt]);
             }
-            xch[ct][half][0][tt][lane] = wsa;
-            xch[ct][half][1][tt][lane] = qsa;
         }
-        __syncthreads();
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) xws[ct][half][tt][lane] = wsa[tt];
+        // Qh S partials of the other half's output tiles ({1, 2} for half 0, {0, 3} for half 1)
+        xqs[ct][half][0][lane] = half ? qsa[0] : qsa[1];
+        xqs[ct][half][1][lane] = half ? qsa[3] : qsa[2];
+        // operands of the second part of the chunk, requested before the barrier
+        auto ldK = [&](int r, int kb2) __attribute__((always_inline)) { return P::ld_plain(sb + L::offK, L::nK, (half * RTH + r) * 2 + kb2, lane); };
+        Plain kf[RTH][2];
+        if (BF16) {
+#pragma unroll
+            for (int r = 0; r < RTH; ++r)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) kf[r][kb2] = ldK(r, kb2);
+        }
+        const Split af0 = P::ld_split(sb + L::offA, L::nA, aidx(ot0, 0), lane);
+        const Split af10 = P::ld_split(sb + L::offA, L::nA, aidx(ot1, 0), lane);
+        const Split af11 = P::ld_split(sb + L::offA, L::nA, aidx(ot1, 1), lane);
+        f32x4 e_cur[RTH];
+#pragma unroll
+        for (int r = 0; r < RTH; ++r)
+            e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (half * RTH + r) + 4 * grp));
+        // exchange barrier: only LDS traffic must be complete (lgkmcnt); copies into the other
+        // stage buffer stay in flight (a fence here would wait for them too)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // Ud = U - (W S [half 0] + W S [half 1])
         f32x4 ud[4];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) ud[tt] = u_cur[tt] - (xch[ct][0][0][tt][lane] + xch[ct][1][0][tt][lane]);
+        for (int tt = 0; tt < 4; ++tt) {
+            const f32x4 oth = xws[ct][half ^ 1][tt][lane];
+            ud[tt] = u_cur[tt] - (half ? oth + wsa[tt] : wsa[tt] + oth);
+        }
         Split Uop[2];
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -698,32 +790,54 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
                              ud[2 * kb2 + 1][0], ud[2 * kb2 + 1][1], ud[2 * kb2 + 1][2], ud[2 * kb2 + 1][3]};
             Uop[kb2] = P::split(vals);
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int tt = i ? ot1 : ot0;
-            f32x4 oa = xch[ct][0][1][tt][lane] + xch[ct][1][1][tt][lane];
-            for (int kb2 = 0; kb2 <= tt / 2; ++kb2)
-                oa = mfma(P::ld_split(sb + L::offA, L::nA, aidx(tt, kb2), lane), Uop[kb2], oa);
-            o_pend[i] = oa;
+        // O rows of tiles ot0 (one Aqk k-block) and ot1 (two)
+        f32x4 oo[2];
+        {
+            const f32x4 q0 = half ? qsa[1] : qsa[0], q1 = half ? qsa[2] : qsa[3];
+            const f32x4 p0 = xqs[ct][half ^ 1][0][lane], p1 = xqs[ct][half ^ 1][1][lane];
+            f32x4 oa0 = half ? p0 + q0 : q0 + p0;
+            f32x4 oa1 = half ? p1 + q1 : q1 + p1;
+            oa0 = mfma(af0, Uop[0], oa0);
+            oa1 = mfma(af10, Uop[0], oa1);
+            oa1 = mfma(af11, Uop[1], oa1);
+            oo[0] = oa0;
+            oo[1] = oa1;
         }
 #pragma unroll
         for (int r = 0; r < RTH; ++r) {
-            const int rt = half * RTH + r;
             f32x4 acc = S[r] * e_cur[r];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
-                acc = mfma(P::ld_plain(sb + L::offK, L::nK, rt * 2 + kb2, lane), Uop[kb2], acc);
+            for (int kb2 = 0; kb2 < 2; ++kb2) acc = mfma(BF16 ? kf[r][kb2] : ldK(r, kb2), Uop[kb2], acc);
             S[r] = acc;
         }
-        o_tok0 = s_tok + c * kChunk;
-        o_Cc = (int)min((long)kChunk, L_n - c * kChunk);
-        if (!St::kDouble && c + 1 < nck) {
-            __syncthreads();  // every wave is done with the single buffer
-            stage_chunk(c + 1, 0);
-            prefetch_regs(c + 1);
+        if (kProd) {
+            // rows of this chunk for the producer (it read the previous ones before the barrier)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    IO<TIO>::store(&obuf[16 * (i ? ot1 : ot0) + 4 * grp + e][0], ct * 16 + r16, scale * oo[i][e]);
+        } else {
+            const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
+            TIO *ob = o + ((s_tok + c * kChunk) * H + h) * (long)D + col;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * (i ? ot1 : ot0) + 4 * grp + e;
+                    if (t < Cc) IO<TIO>::store(ob, (long)t * HD, scale * oo[i][e]);
+                }
+            if (more) {
+                __syncthreads();  // every wave is done with the single buffer
+                stage_all(c + 1);
+            }
         }
+    };
+    for (long c = 0; c < nck; c += 2) {
+        chunk_step(c, I0{}, uA, uB);
+        if (c + 1 < nck) chunk_step(c + 1, std::integral_constant<int, kProd ? 1 : 0>{}, uB, uA);
     }
-    if (nck > 0) store_out();
+    if (kProd) __syncthreads();  // hands the last chunk's rows to the producer
     if (sN) {
 #pragma unroll
         for (int r = 0; r < RTH; ++r)
@@ -759,7 +873,7 @@ template <bool BF16, int D, int NCT>
 static hipError_t launch_scan_nct(const FwdArgs &a, hipStream_t st, int nchains) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NCT);
-    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT>), dim3((unsigned)blocks), dim3(128 * NCT), 0, st,
+    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT>), dim3((unsigned)blocks), dim3(scan_threads<BF16, D, NCT>()), 0, st,
                        a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale, a.s0, a.sN, (TIO *)a.o, (const char *)a.ws);
     return hipGetLastError();
 }
