@@ -555,22 +555,26 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 // bit-identical Ud.  Each wave then updates its own state rows and forms two of the four
 // 16-token output tiles.
 // The operands shared by all tiles (W, Qh, Kh^T, Aqk, e^gamma: one contiguous block at the start
-// of the chunk's workspace record) are copied into LDS by direct global->LDS loads.  When two
-// copies fit in LDS, one extra wave per workgroup (the producer) copies chunk c+1 while the
-// compute waves work on chunk c, and also writes the output rows, which the compute waves leave
-// in LDS: a wave stalls while the memory pipeline accepts its loads, and this keeps those
-// stalls off the waves that issue the MFMAs.  Otherwise the compute waves copy the next chunk
-// themselves after the current one.  U goes to registers one chunk ahead.
+// of the chunk's workspace record) are copied into LDS by direct global->LDS loads.  Every read
+// of a chunk's block is complete at that chunk's exchange barrier, so with two buffers the copy
+// of chunk c+2 can start right after the exchange barrier of chunk c and has most of two chunk
+// bodies to land.  Two extra waves per workgroup (producers: one for the even chunks, one for
+// the odd ones, so each has at most one chunk in flight and waits for it with vmcnt(0)) issue
+// these copies: a wave stalls while the memory pipeline accepts its loads, and this keeps
+// those stalls off the waves that issue the MFMAs.  When two buffers do not fit, the compute waves copy the next chunk
+// themselves after the current one.  U goes to registers one chunk ahead.  Output rows are
+// left in LDS and written after the next barrier with 16-byte stores.
 template <bool BF16, int D> struct ScanStage {
     using L = WsLayout<BF16, D>;
     static constexpr size_t bytes = L::offU;                     // W, Qh, Kh^T, Aqk, e^gamma
     static constexpr int kLoads = (int)(bytes / 1024);           // one 1 KB wave-load each
-    static constexpr bool kProducer = 2 * bytes <= 128 * 1024;   // double buffer + producer wave
+    static constexpr bool kProducer = 2 * bytes <= 128 * 1024;   // double buffer + producer waves
+    static constexpr int kNP = kProducer ? 2 : 0;                // producer waves per workgroup
     static_assert(bytes % 1024 == 0, "staged block is a whole number of wave-loads");
 };
 
 template <bool BF16, int D, int NCT>
-constexpr int scan_threads() { return 64 * (2 * NCT + (ScanStage<BF16, D>::kProducer ? 1 : 0)); }
+constexpr int scan_threads() { return 64 * (2 * NCT + ScanStage<BF16, D>::kNP); }
 
 template <bool BF16, int D, int NCT>
 __global__ void __launch_bounds__((scan_threads<BF16, D, NCT>()))
@@ -588,7 +592,6 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     constexpr int KBH = NKB / 2, RTH = NRT / 2;  // k-blocks and row tiles per half
     constexpr int NW = 2 * NCT;                  // compute waves
     constexpr int LPW = (St::kLoads + NW - 1) / NW;  // copies per compute wave (no producer)
-    constexpr int kCopyA = (St::kLoads + 1) / 2;     // producer copies issued before the exchange
     constexpr int OC = NCT * 16;                     // output columns of the workgroup
     static_assert(GPC * NCT == NJT && KBH >= 1, "tiling");
     // two separate arrays (not one [2][bytes] array) so that alias analysis can tell a read of
@@ -598,6 +601,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     __shared__ f32x4 xws[NCT][2][4][64];  // [tile][from half][token tile][lane]: W S partials
     __shared__ f32x4 xqs[NCT][2][2][64];  // Qh S partials of the receiving half's output tiles
     __shared__ __attribute__((aligned(16))) TIO obuf[kProd ? kChunk : 1][kProd ? OC : 1];  // output rows
+    static_assert(!kProd || (kChunk * OC * (int)sizeof(TIO)) % (NW * 1024) == 0, "row stores split evenly");
 
     // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
     const int b = blockIdx.x, xcd = b & 7, sl = b >> 3;
@@ -605,7 +609,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     if (chain >= nchains) return;  // uniform over the workgroup
     const int n = chain / H, h = chain % H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
-    const bool producer = kProd && wave == NW;
+    const bool producer = kProd && wave >= NW;
     const int ct = producer ? 0 : wave >> 1, half = wave & 1;
     const int jt = jg * NCT + ct;
     const int col = 16 * jt + r16;
@@ -634,52 +638,54 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 
     // ================================================================ producer wave
     if (producer) {
-        // wave-loads I0 <= i < I1 of chunk c into buffer BUF
-        auto copy_part = [&](long c, auto bufc, auto i0c, auto i1c) __attribute__((always_inline)) {
+        // all wave-loads of chunk c into buffer BUF
+        auto copy_chunk = [&](long c, auto bufc) __attribute__((always_inline)) {
             char *dst = decltype(bufc)::value ? stage1 : stage0;
             const char *src = record(c);
 #pragma unroll
-            for (int i = decltype(i0c)::value; i < decltype(i1c)::value; ++i) copy_one(src, dst, i);
+            for (int i = 0; i < St::kLoads; ++i) copy_one(src, dst, i);
         };
-        // output rows of chunk c: 16 bytes per lane, RPI token rows per instruction
-        auto store_rows = [&](long c) __attribute__((always_inline)) {
-            constexpr int LPR = OC * (int)sizeof(TIO) / 16, RPI = 64 / LPR, EPL = 16 / (int)sizeof(TIO);
-            static_assert(LPR * RPI == 64, "row split");
-            const long tok0 = s_tok + c * kChunk;
-            const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
-            const int r0 = lane / LPR, part = lane % LPR;
-            TIO *dst = o + (tok0 * H + h) * (long)D + jg * OC + part * EPL;
-#pragma unroll
-            for (int k = 0; k < kChunk / RPI; ++k) {
-                const int t = k * RPI + r0;
-                const uint4 val = *reinterpret_cast<const uint4 *>(&obuf[t][part * EPL]);
-                if (t < Cc) *reinterpret_cast<uint4 *>(dst + (long)t * HD) = val;
-            }
-        };
-        using KA = std::integral_constant<int, kCopyA>;
-        using KL = std::integral_constant<int, St::kLoads>;
-        if (nck > 0) copy_part(0, I0{}, I0{}, KL{});
+        const int pw = wave - NW;  // this producer copies the chunks c with c % 2 == pw
+        if (pw < nck) {
+            if (pw == 0) copy_chunk(0, I0{});
+            else copy_chunk(1, I1{});
+        }
         auto pstep = [&](long c, auto bufc) __attribute__((always_inline)) {
-            using NB = std::integral_constant<int, decltype(bufc)::value ^ 1>;
-            __builtin_amdgcn_s_waitcnt(0);  // copies of chunk c have landed
-            __syncthreads();
-            const bool more = c + 1 < nck;
-            if (c > 0) store_rows(c - 1);   // rows left in obuf before this barrier
-            if (more) copy_part(c + 1, NB{}, I0{}, KA{});
-            // exchange barrier (obuf has been read: the compute waves refill it after this)
+            constexpr int buf = decltype(bufc)::value;
+            const bool mine = buf == pw;  // chunk c's parity is buf
+            if (mine) __builtin_amdgcn_s_waitcnt(0);  // this producer's copies of chunk c landed
+            // top barrier without a fence (a fence would make the other producer wait for its
+            // copies of the next chunk too)
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (more) copy_part(c + 1, NB{}, KA{}, KL{});
+            // exchange barrier: past it, no wave reads this chunk's buffer any more
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            if (mine && c + 2 < nck) copy_chunk(c + 2, bufc);
         };
         for (long c = 0; c < nck; c += 2) {
             pstep(c, I0{});
             if (c + 1 < nck) pstep(c + 1, I1{});
         }
-        __syncthreads();  // the last chunk's rows are in obuf
-        if (nck > 0) store_rows(nck - 1);
+        __syncthreads();  // pairs with the compute waves' last barrier
         return;
     }
 
     // ================================================================ compute waves
+    // output rows of chunk c from obuf, 16 bytes per lane; compute wave w takes row blocks
+    // w, w + NW, ... of RPI rows each
+    auto store_rows = [&](long c) __attribute__((always_inline)) {
+        constexpr int LPR = OC * (int)sizeof(TIO) / 16, RPI = 64 / LPR, EPL = 16 / (int)sizeof(TIO);
+        static_assert(LPR * RPI == 64 && (kChunk / RPI) % NW == 0, "row split");
+        const long tok0 = s_tok + c * kChunk;
+        const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
+        const int r0 = lane / LPR, part = lane % LPR;
+        TIO *dst = o + (tok0 * H + h) * (long)D + jg * OC + part * EPL;
+#pragma unroll
+        for (int kk = 0; kk < kChunk / RPI / NW; ++kk) {
+            const int t = (kk * NW + wave) * RPI + r0;
+            const uint4 val = *reinterpret_cast<const uint4 *>(&obuf[t][part * EPL]);
+            if (t < Cc) *reinterpret_cast<uint4 *>(dst + (long)t * HD) = val;
+        }
+    };
     // this wave's share of the copies of chunk c (no producer wave): wave-load j * NW + wave
     auto stage_all = [&](long c) __attribute__((always_inline)) {
 #pragma unroll
@@ -758,9 +764,12 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         xqs[ct][half][0][lane] = half ? qsa[0] : qsa[1];
         xqs[ct][half][1][lane] = half ? qsa[3] : qsa[2];
         // operands of the second part of the chunk, requested before the barrier
+        // (with a producer the buffer is refilled right after the exchange barrier, so every
+        // read of it must be issued before; without one, fp32 fragments are read next to use)
+        constexpr bool kEarlyK = BF16 || kProd;
         auto ldK = [&](int r, int kb2) __attribute__((always_inline)) { return P::ld_plain(sb + L::offK, L::nK, (half * RTH + r) * 2 + kb2, lane); };
         Plain kf[RTH][2];
-        if (BF16) {
+        if (kEarlyK) {
 #pragma unroll
             for (int r = 0; r < RTH; ++r)
 #pragma unroll
@@ -773,6 +782,9 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
         for (int r = 0; r < RTH; ++r)
             e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (half * RTH + r) + 4 * grp));
+        // rows of the previous chunk (left in obuf before the top barrier; refilled after the
+        // exchange barrier)
+        if (kProd && c > 0) store_rows(c - 1);
         // exchange barrier: only LDS traffic must be complete (lgkmcnt); copies into the other
         // stage buffer stay in flight (a fence here would wait for them too)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -807,11 +819,11 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         for (int r = 0; r < RTH; ++r) {
             f32x4 acc = S[r] * e_cur[r];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) acc = mfma(BF16 ? kf[r][kb2] : ldK(r, kb2), Uop[kb2], acc);
+            for (int kb2 = 0; kb2 < 2; ++kb2) acc = mfma(kEarlyK ? kf[r][kb2] : ldK(r, kb2), Uop[kb2], acc);
             S[r] = acc;
         }
         if (kProd) {
-            // rows of this chunk for the producer (it read the previous ones before the barrier)
+            // rows of this chunk (the previous ones were read before the exchange barrier)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -837,7 +849,10 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         chunk_step(c, I0{}, uA, uB);
         if (c + 1 < nck) chunk_step(c + 1, std::integral_constant<int, kProd ? 1 : 0>{}, uB, uA);
     }
-    if (kProd) __syncthreads();  // hands the last chunk's rows to the producer
+    if (kProd) {
+        __syncthreads();  // the last chunk's rows are in obuf
+        if (nck > 0) store_rows(nck - 1);
+    }
     if (sN) {
 #pragma unroll
         for (int r = 0; r < RTH; ++r)
