@@ -27,6 +27,7 @@
 // Precision (bf16 inputs).  The Gram operands, Tm, Aqk, S and Ud enter the MFMAs as hi + lo
 // bf16 pairs (about 16 significant bits); U stays fp32.  q, k, v are used as stored (exact).
 // The fp32 path uses fp32 MFMAs throughout.
+#include <atomic>
 #include <type_traits>
 
 #include "kda_common.h"
@@ -893,17 +894,28 @@ static hipError_t launch_scan_nct(const FwdArgs &a, hipStream_t st, int nchains)
     return hipGetLastError();
 }
 
+// Compute units of the current device, queried once per device (the value never changes).
+static int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+    if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
 // Column tiles per workgroup: two when that still gives every CU a workgroup (the tiles then
 // share one LDS copy of the chunk's operands), else one.
 template <bool BF16, int D>
 static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
     const int nchains = a.N * a.H;
     if (nchains <= 0) return hipSuccess;
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
+    const int cus = device_cu_count();
     const long tiles = (long)nchains * (D / 16);
     if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2>(a, st, nchains);
     return launch_scan_nct<BF16, D, 1>(a, st, nchains);
