@@ -151,7 +151,23 @@ __device__ __forceinline__ ChunkPos locate_chunk(long slot, const int32_t *cu, i
 }
 
 // ------------------------------------------------------------------ kernel 1: chunk-local
-template <bool BF16, int D> struct ChunkSmem {
+// The 8 k-slot values of one LDS row for lane group grp: elements 32 kb + kslot(grp, s), read
+// as two runs of 4 consecutive elements (rows and runs are 16-byte aligned for fp32, 8-byte for
+// bf16).
+__device__ __forceinline__ void ld_kslots(const float *row, int kb, int grp, float *out) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(row + 32 * kb + 4 * grp);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(row + 32 * kb + 16 + 4 * grp);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { out[u] = a[u]; out[4 + u] = b[u]; }
+}
+__device__ __forceinline__ void ld_kslots(const uint16_t *row, int kb, int grp, float *out) {
+    const f32x4 a = load4(row + 32 * kb + 4 * grp);
+    const f32x4 b = load4(row + 32 * kb + 16 + 4 * grp);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { out[u] = a[u]; out[4 + u] = b[u]; }
+}
+
+template <bool BF16, int D> struct alignas(16) ChunkSmem {
     using TIO = typename std::conditional<BF16, uint16_t, float>::type;
     static constexpr int GS = D + 4, KS = D + 8, VS = kChunk + 8, AS = kChunk + 4;
     static constexpr int CQ = D / 4;          // channel quads
@@ -297,13 +313,14 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             const int t = 16 * tt + r16, m = mid_row(tt);
-            float vals[8];
+            float gt[8], gm[8], vals[8];
+            ld_kslots(&sm.g.G[t][0], kb, grp, gt);
+            ld_kslots(&sm.g.G[m][0], kb, grp, gm);
+            ld_kslots(&sm.kq.in.Q[t][0], kb, grp, vals);
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
-                const int c = 32 * kb + kslot(grp, s);
-                const float gt = sm.g.G[t][c];
-                span_bad |= fabsf(gt - sm.g.G[m][c]) > 115.f;
-                vals[s] = IO<TIO>::load(&sm.kq.in.Q[t][0], c) * fast_exp2(gt);
+                span_bad |= fabsf(gt[s] - gm[s]) > 115.f;
+                vals[s] *= fast_exp2(gt[s]);
             }
             P::st_plain(wsQ, L::nQ, tt * NKB + kb, lane, P::plain(vals));
         }
@@ -348,42 +365,56 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
             for (int kk = 0; kk < KBW; ++kk) {
                 const int kb = ch * KBW + kk;
                 // row factors of the blocks this group uses: pairs (0,0) (1,0) (1,1) (2,0) (2,1) for
-                // group 0, (2,2) (3,0) (3,1) (3,2) (3,3) for group 1
-                float kA[4][8], qA[4][8], kB[4][8];
+                // group 0, (2,2) (3,0) (3,1) (3,2) (3,3) for group 1.  The A side (k_i, q_i times
+                // e^{G_i - G_mI}) is split once per block row and shared by the block's pairs; the
+                // bridge e^{G_mI - G_mJ} of an off-diagonal pair scales the B side
+                // (k_j e^{G_mJ - G_j}), which is split per pair.
+                Split sK[4], sQ[4];
+                float kB[4][8];
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     const bool needA = PG == 0 ? I <= 2 : I >= 2;
                     const bool needB = PG == 0 ? I <= 1 : true;
                     if (!needA && !needB) continue;
                     const int i = 16 * I + r16, m = mid_row(I);
+                    float gi[8], gm[8], kv[8];
+                    ld_kslots(&sm.g.G[i][0], kb, grp, gi);
+                    ld_kslots(&sm.g.G[m][0], kb, grp, gm);
+                    ld_kslots(&sm.kq.in.K[i][0], kb, grp, kv);
+                    if (needA) {
+                        float qv[8], ka[8], qa[8];
+                        ld_kslots(&sm.kq.in.Q[i][0], kb, grp, qv);
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        const int c = 32 * kb + kslot(grp, s);
-                        const float d = sm.g.G[i][c] - sm.g.G[m][c];
-                        const float kv = IO<TIO>::load(&sm.kq.in.K[i][0], c);
-                        if (needA) {
-                            const float fa = fast_exp2(d);
-                            kA[I][s] = kv * fa;
-                            qA[I][s] = IO<TIO>::load(&sm.kq.in.Q[i][0], c) * fa;
+                        for (int s = 0; s < 8; ++s) {
+                            const float fa = fast_exp2(gi[s] - gm[s]);
+                            ka[s] = kv[s] * fa;
+                            qa[s] = qv[s] * fa;
                         }
-                        if (needB) kB[I][s] = kv * fast_exp2(-d);
+                        sK[I] = P::split(ka);
+                        sQ[I] = P::split(qa);
+                    }
+                    if (needB) {
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) kB[I][s] = kv[s] * fast_exp2(gm[s] - gi[s]);
                     }
                 }
 #pragma unroll
                 for (int u = 0; u < 5; ++u) {
                     int I, J;
                     pair_ij(PG * 5 + u, I, J);
-                    float ak[8], aq[8];
+                    float bv[8];
+                    if (I > J) {
+                        float br[8];
+                        ld_kslots(&sm.bridge[bridge_idx(I, J)][0], kb, grp, br);
 #pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        float br = 1.f;
-                        if (I > J) br = sm.bridge[bridge_idx(I, J)][32 * kb + kslot(grp, s)];
-                        ak[s] = kA[I][s] * br;
-                        aq[s] = qA[I][s] * br;
+                        for (int s = 0; s < 8; ++s) bv[s] = kB[J][s] * br[s];
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < 8; ++s) bv[s] = kB[J][s];
                     }
-                    const Split bop = P::split(kB[J]);
-                    accK[u] = mfma(P::split(ak), bop, accK[u]);
-                    accQ[u] = mfma(P::split(aq), bop, accQ[u]);
+                    const Split bop = P::split(bv);
+                    accK[u] = mfma(sK[I], bop, accK[u]);
+                    accQ[u] = mfma(sQ[I], bop, accQ[u]);
                 }
             }
         };
@@ -486,20 +517,27 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     // W = T' X and U = T' V.
     for (int f = wave; f < 6; f += 4) {  // Aqk fragments
         const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
+        const int t = 16 * tt + r16;
         float vals[8];
+        ld_kslots(&sm.kq.a.Aqk[t][0], kb2, grp, vals);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int t = 16 * tt + r16, tp = 32 * kb2 + kslot(grp, s);
-            vals[s] = tp <= t ? sm.kq.a.Aqk[t][tp] : 0.f;  // causal mask, incl. the diagonal
-        }
+        for (int s = 0; s < 8; ++s)  // causal mask, incl. the diagonal (entries above were never written)
+            if (32 * kb2 + kslot(grp, s) > t) vals[s] = 0.f;
         P::st_split(wsA, L::nA, f, lane, P::split(vals));
     }
     __syncthreads();  // Akk, Aqk are dead from here on
 #pragma unroll
-    for (int r = 0; r < RPG; ++r) {
-        const int t = rg * RPG + r;
+    for (int u = 0; u < 4; ++u) {  // channel c4 + u: RPG consecutive tokens, one vector store
+        union { TIO e[RPG]; uint4 q[(RPG * sizeof(TIO) + 15) / 16]; uint2 d; } col;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) sm.kq.VT[c4 + u][t] = vv[r].elem(u);
+        for (int r = 0; r < RPG; ++r) col.e[r] = vv[r].elem(u);
+        TIO *dst = &sm.kq.VT[c4 + u][rg * RPG];
+        if constexpr (RPG * sizeof(TIO) == 8) {
+            *reinterpret_cast<uint2 *>(dst) = col.d;
+        } else {
+#pragma unroll
+            for (int w = 0; w < (int)(RPG * sizeof(TIO) / 16); ++w) reinterpret_cast<uint4 *>(dst)[w] = col.q[w];
+        }
     }
     __syncthreads();
     // T' = Tm Diag(beta) fragments; the same values serve as the A operand (row t, k = t')
@@ -508,13 +546,12 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 #pragma unroll
     for (int f = 0; f < 6; ++f) {
         const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
-        float vals[8];
+        float vals[8], bv[8];
+        ld_kslots(&sm.g.T[16 * tt + r16][0], kb2, grp, vals);
+        ld_kslots(&sm.beta[0], kb2, grp, bv);
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int tp = 32 * kb2 + kslot(grp, s);
-            // Tm is zero above its 16x16 diagonal blocks (those entries are never written)
-            vals[s] = (tp >> 4) <= tt ? sm.g.T[16 * tt + r16][tp] * sm.beta[tp] : 0.f;
-        }
+        for (int s = 0; s < 8; ++s)  // Tm is zero above its 16x16 diagonal blocks (never written)
+            vals[s] = ((32 * kb2 + kslot(grp, s)) >> 4) <= tt ? vals[s] * bv[s] : 0.f;
         Tf[f] = P::split(vals);
     }
     for (int kb = wave; kb < NKB; kb += 4) {  // W fragments (tt, kb)
@@ -534,8 +571,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
             float vals[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) vals[s] = IO<TIO>::load(&sm.kq.VT[16 * jt + r16][0], 32 * kb2 + kslot(grp, s));
+            ld_kslots(&sm.kq.VT[16 * jt + r16][0], kb2, grp, vals);
             Vf[kb2] = P::plain(vals);
         }
 #pragma unroll
