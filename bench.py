@@ -7,10 +7,12 @@ The same run also measures
     100 consecutive steps): state GB/s and fraction of HBM peak;
   * the q/k prologue on the packed 64-sequence batch (lengths U[512, 16384], H = 32):
     GB/s;
+  * the long-context prefill (B = 1, H = 32, T = 131072) and the varlen layer (prologue on q
+    and k, then the prefill of the packed 64-sequence batch): ms and tokens/s;
   * the fp64 CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel times come from HIP events recorded on the stream the kernels run on.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,cpu,copy]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,long,varlen,cpu,copy]
 Prints one JSON line.  `--only copy` runs a plain 256 MiB device copy (a kernel of known size
 used to calibrate the FETCH_SIZE / WRITE_SIZE counters of profiler runs).
 The roofline "traffic" figure comes from profiles/traffic.json (counter runs of this same
@@ -181,6 +183,104 @@ def bench_prep(args, torch, kda, dev):
     return dict(ms=ms, tokens=ntok, bytes=nbytes, gbs=nbytes / ms / 1e6)
 
 
+def _unit_bf16(x):
+    import torch
+    return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+
+def bench_long(torch, kda, dev, reps=5):
+    """Long-context prefill: B=1, H=32, T=131072, d=128, S_0 ~ N(0, 0.02), one kda_fwd per rep
+    (inputs drawn on the GPU with the same distributions as the parity tests)."""
+    B, T, H, d = 1, 131072, 32, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93002)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    q, k = _unit_bf16(rnd(B, T, H, d)), _unit_bf16(rnd(B, T, H, d))
+    v = rnd(B, T, H, d).to(torch.bfloat16)
+    beta = torch.sigmoid(rnd(B, T, H))
+    g = -torch.nn.functional.softplus(rnd(B, T, H, d) + 2)
+    S0 = rnd(B, H, d, d) * 0.02
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    S = torch.empty_like(S0)
+    nws = kda.fwd_workspace_bytes(kda.KDA_BF16, B, T, H, d, d, B, False)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    L = kda.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+
+    def step():
+        assert L.kda_fwd(kda.KDA_BF16, B, T, H, d, d, None, B, p(q), p(k), p(v), p(g), p(beta), 1.0, p(S0),
+                         p(S), p(o), p(ws), nws, st) == 0
+
+    def local():
+        assert L.kda_fwd_chunk_local(kda.KDA_BF16, B, T, H, d, d, None, B, p(q), p(k), p(v), p(g), p(beta),
+                                     p(ws), nws, st) == 0
+
+    def scan():
+        assert L.kda_fwd_state_scan(kda.KDA_BF16, B, T, H, d, d, None, B, 1.0, p(S0), p(S), p(o), p(ws), nws,
+                                    st) == 0
+
+    step()
+    torch.cuda.synchronize()
+    ms = time_events(step, reps, torch)
+    ms_local = time_events(local, reps, torch)
+    ms_scan = time_events(scan, reps, torch)
+    th = B * T * H
+    return {"workload": "KDA prefill B=1 H=32 T=131072 d=128, bf16 q/k/v, S_0 ~ N(0, 0.02)",
+            "ms": ms, "ms_chunk_local": ms_local, "ms_state_scan": ms_scan, "tokens_per_s": B * T / (ms / 1e3),
+            "algorithmic_GBs": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * th / ms / 1e6,
+            "hbm_frac": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * th / ms / 1e6 / HBM_PEAK_GBS}
+
+
+def bench_varlen_layer(torch, kda, dev, reps=5):
+    """Varlen layer: 64 packed sequences (lengths U[512, 16384] from the workload seed), H=32, d=128:
+    prologue on raw q and k (width 4), then the chunked prefill with per-sequence S_0 ~ N(0, 0.02)."""
+    import kda_inputs as ki
+    lengths = ki.config4_lengths()
+    H, d = 32, 128
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T, N = int(cu[-1]), len(lengths)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93004)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    qr, kr = rnd(1, T, H, d).to(torch.bfloat16), rnd(1, T, H, d).to(torch.bfloat16)
+    v = rnd(1, T, H, d).to(torch.bfloat16)
+    beta = torch.sigmoid(rnd(1, T, H))
+    g = -torch.nn.functional.softplus(rnd(1, T, H, d) + 2)
+    wq, wk = (rnd(H * d, 4) * 0.5).contiguous(), (rnd(H * d, 4) * 0.5).contiguous()
+    S0 = rnd(N, H, d, d) * 0.02
+    cu_d = torch.from_numpy(cu).to(dev)
+    q, k = torch.empty_like(qr), torch.empty_like(kr)
+    o = torch.empty_like(v)
+    S = torch.empty_like(S0)
+    nws = kda.fwd_workspace_bytes(kda.KDA_BF16, 1, T, H, d, d, N, True)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    L = kda.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+
+    def layer():
+        assert L.kda_prep(kda.KDA_BF16, 1, T, H, d, p(cu_d), N, p(qr), p(wq), 4, p(q), st) == 0
+        assert L.kda_prep(kda.KDA_BF16, 1, T, H, d, p(cu_d), N, p(kr), p(wk), 4, p(k), st) == 0
+        assert L.kda_fwd(kda.KDA_BF16, 1, T, H, d, d, p(cu_d), N, p(q), p(k), p(v), p(g), p(beta), 1.0, p(S0),
+                         p(S), p(o), p(ws), nws, st) == 0
+
+    def fwd():
+        assert L.kda_fwd(kda.KDA_BF16, 1, T, H, d, d, p(cu_d), N, p(q), p(k), p(v), p(g), p(beta), 1.0, p(S0),
+                         p(S), p(o), p(ws), nws, st) == 0
+
+    layer()
+    torch.cuda.synchronize()
+    ms = time_events(layer, reps, torch)
+    ms_fwd = time_events(fwd, reps, torch)
+    th = T * H
+    return {"workload": f"{T} packed tokens (64 sequences, lengths U[512, 16384]), H=32, d=128: 2 prologue "
+                        "launches (q, k) + chunked prefill with per-sequence S_0",
+            "ms_layer": ms, "ms_fwd": ms_fwd, "tokens_per_s": T / (ms / 1e3),
+            "fwd_algorithmic_GBs": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * th / ms_fwd / 1e6}
+
+
 def cpu_baseline(inp, min_seconds=10.0):
     """The fp64 oracle on the prefill batch, repeated whole passes until ~10 s of wall time."""
     import oracle
@@ -239,8 +339,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,prep,cpu",
-                    help="comma list of prefill, decode, prep, cpu, copy")
+    ap.add_argument("--only", default="prefill,decode,prep,long,varlen,cpu",
+                    help="comma list of prefill, decode, prep, long, varlen, cpu, copy")
     args = ap.parse_args()
     only = set(x.strip() for x in args.only.split(",") if x.strip())
     if args.gpus != 1:
@@ -314,6 +414,12 @@ def main():
         pr = bench_prep(args, torch, kda, dev)
         out["prep"] = {"workload": f"{pr['tokens']} packed tokens (64 sequences), H=32, d=128, width 4, bf16",
                        "ms": pr["ms"], "GBs": pr["gbs"], "frac": pr["gbs"] / HBM_PEAK_GBS}
+    if "long" in only:
+        log("long context ...")
+        out["long_context"] = bench_long(torch, kda, dev)
+    if "varlen" in only:
+        log("varlen layer ...")
+        out["varlen_layer"] = bench_varlen_layer(torch, kda, dev)
     if "copy" in only:
         out["copy"] = bench_copy(torch, dev)
     if "cpu" in only:

@@ -585,12 +585,13 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
 }
 
 // ------------------------------------------------------------------ kernel 2: state scan
-// A workgroup serves NCT tiles of 16 value columns of one (sequence, head) chain with two waves
-// per tile: wave `half` keeps rows half*D/2 .. of the tile's fp32 state in accumulator registers.
-// Per chunk each wave forms its half of W S and Qh S and hands the other wave, through LDS, the
-// partial sums that wave needs; both add the halves as (half 0) + (half 1), so both hold
-// bit-identical Ud.  Each wave then updates its own state rows and forms two of the four
-// 16-token output tiles.
+// A workgroup serves NCT tiles of 16 value columns of one (sequence, head) chain with NS waves
+// per tile (NS = 2 or 4): wave `part` keeps rows part*D/NS .. of the tile's fp32 state in
+// accumulator registers.  Per chunk each wave forms its part of W S and Qh S and publishes them
+// in LDS; every wave adds the parts in the fixed order part 0 + part 1 + ..., so all hold
+// bit-identical Ud.  Each wave then updates its own state rows and forms 4 / NS of the four
+// 16-token output tiles.  Four parts shorten the serial chain per chunk; they are used when the
+// problem has too few tiles to fill the GPU with two-part workgroups.
 // The operands shared by all tiles (W, Qh, Kh^T, Aqk, e^gamma: one contiguous block at the start
 // of the chunk's workspace record) are copied into LDS by direct global->LDS loads.  Every read
 // of a chunk's block is complete at that chunk's exchange barrier, so with two buffers the copy
@@ -610,11 +611,11 @@ template <bool BF16, int D> struct ScanStage {
     static_assert(bytes % 1024 == 0, "staged block is a whole number of wave-loads");
 };
 
-template <bool BF16, int D, int NCT>
-constexpr int scan_threads() { return 64 * (2 * NCT + ScanStage<BF16, D>::kNP); }
+template <bool BF16, int D, int NCT, int NS>
+constexpr int scan_threads() { return 64 * (NS * NCT + ScanStage<BF16, D>::kNP); }
 
-template <bool BF16, int D, int NCT>
-__global__ void __launch_bounds__((scan_threads<BF16, D, NCT>()))
+template <bool BF16, int D, int NCT, int NS>
+__global__ void __launch_bounds__((scan_threads<BF16, D, NCT, NS>()))
 chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
                   const float *__restrict__ s0, float *__restrict__ sN,
                   typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws) {
@@ -626,19 +627,20 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     using Split = typename P::Split;
     constexpr bool kProd = St::kProducer;
     constexpr int NKB = L::NKB, NRT = L::NRT, NJT = D / 16, GPC = NJT / NCT;
-    constexpr int KBH = NKB / 2, RTH = NRT / 2;  // k-blocks and row tiles per half
-    constexpr int NW = 2 * NCT;                  // compute waves
+    constexpr int KBH = NKB / NS, RTH = NRT / NS;  // k-blocks and row tiles per part
+    constexpr int NW = NS * NCT;                   // compute waves
+    constexpr int NOT = 4 / NS;                    // output token tiles per wave
     constexpr int LPW = (St::kLoads + NW - 1) / NW;  // copies per compute wave (no producer)
     constexpr int OC = NCT * 16;                     // output columns of the workgroup
-    static_assert(GPC * NCT == NJT && KBH >= 1, "tiling");
+    static_assert(GPC * NCT == NJT && KBH >= 1 && KBH * NS == NKB && (NS == 2 || NS == 4), "tiling");
     // two separate arrays (not one [2][bytes] array) so that alias analysis can tell a read of
     // one buffer from an in-flight copy into the other
     __shared__ __attribute__((aligned(16))) char stage0[St::bytes];
     __shared__ __attribute__((aligned(16))) char stage1[kProd ? St::bytes : 16];
-    __shared__ f32x4 xws[NCT][2][4][64];  // [tile][from half][token tile][lane]: W S partials
-    __shared__ f32x4 xqs[NCT][2][2][64];  // Qh S partials of the receiving half's output tiles
+    __shared__ f32x4 xws[NCT][NS][4][64];  // [tile][from part][token tile][lane]: W S partials
+    // Qh S partials of the tiles a part does not own: [tile][from part][slot][lane]
+    __shared__ f32x4 xqs[NCT][NS][4 - NOT][64];
     __shared__ __attribute__((aligned(16))) TIO obuf[kProd ? kChunk : 1][kProd ? OC : 1];  // output rows
-    static_assert(!kProd || (kChunk * OC * (int)sizeof(TIO)) % (NW * 1024) == 0, "row stores split evenly");
 
     // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
     const int b = blockIdx.x, xcd = b & 7, sl = b >> 3;
@@ -647,11 +649,21 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     const int n = chain / H, h = chain % H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
     const bool producer = kProd && wave >= NW;
-    const int ct = producer ? 0 : wave >> 1, half = wave & 1;
+    const int ct = producer ? 0 : wave / NS, part = wave % NS;
     const int jt = jg * NCT + ct;
     const int col = 16 * jt + r16;
-    // output token tiles of this wave: {0, 3} for half 0, {1, 2} for half 1 (equal MFMA work)
-    const int ot0 = half ? 1 : 0, ot1 = half ? 2 : 3;
+    // output token tiles of this wave: with two parts {0, 3} and {1, 2} (equal MFMA work), with
+    // four parts tile `part`
+    auto own_tile = [&](int i) __attribute__((always_inline)) {
+        return NS == 4 ? part : (part ? (i ? 2 : 1) : (i ? 3 : 0));
+    };
+    auto owns = [&](int pp, int tt) __attribute__((always_inline)) {
+        return NS == 4 ? tt == pp : (pp ? (tt == 1 || tt == 2) : (tt == 0 || tt == 3));
+    };
+    // slot of token tile tt among the tiles part pp does not own
+    auto qslot = [&](int pp, int tt) __attribute__((always_inline)) {
+        return NS == 4 ? (tt < pp ? tt : max(tt - 1, 0)) : (tt >> 1);
+    };
 
     long s_tok, L_n, slot0;
     if (cu) {
@@ -711,16 +723,20 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     // w, w + NW, ... of RPI rows each
     auto store_rows = [&](long c) __attribute__((always_inline)) {
         constexpr int LPR = OC * (int)sizeof(TIO) / 16, RPI = 64 / LPR, EPL = 16 / (int)sizeof(TIO);
-        static_assert(LPR * RPI == 64 && (kChunk / RPI) % NW == 0, "row split");
+        constexpr int NBLK = kChunk / RPI;
+        static_assert(LPR * RPI == 64, "row split");
         const long tok0 = s_tok + c * kChunk;
         const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
-        const int r0 = lane / LPR, part = lane % LPR;
-        TIO *dst = o + (tok0 * H + h) * (long)D + jg * OC + part * EPL;
+        const int r0 = lane / LPR, seg = lane % LPR;
+        TIO *dst = o + (tok0 * H + h) * (long)D + jg * OC + seg * EPL;
 #pragma unroll
-        for (int kk = 0; kk < kChunk / RPI / NW; ++kk) {
-            const int t = (kk * NW + wave) * RPI + r0;
-            const uint4 val = *reinterpret_cast<const uint4 *>(&obuf[t][part * EPL]);
-            if (t < Cc) *reinterpret_cast<uint4 *>(dst + (long)t * HD) = val;
+        for (int kk = 0; kk < (NBLK + NW - 1) / NW; ++kk) {
+            const int blk = kk * NW + wave;
+            if (blk < NBLK) {
+                const int t = blk * RPI + r0;
+                const uint4 val = *reinterpret_cast<const uint4 *>(&obuf[t][seg * EPL]);
+                if (t < Cc) *reinterpret_cast<uint4 *>(dst + (long)t * HD) = val;
+            }
         }
     };
     // this wave's share of the copies of chunk c (no producer wave): wave-load j * NW + wave
@@ -746,7 +762,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     for (int r = 0; r < RTH; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            S[r][e] = s0 ? s0[sbase + (long)(16 * (half * RTH + r) + 4 * grp + e) * D + col] : 0.f;
+            S[r][e] = s0 ? s0[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] : 0.f;
 
     if (nck > 0) {
         if (!kProd) stage_all(0);
@@ -761,10 +777,10 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         __syncthreads();                // ... and every copy: chunk c is in LDS
         const bool more = c + 1 < nck;
         const char *sb = buf ? stage1 : stage0;
-        // W and Qh fragments of this half; bf16 ones are all requested before the first product
+        // W and Qh fragments of this part; bf16 ones are all requested before the first product
         // (fp32 ones take twice the registers and are read next to their use)
-        auto ldW = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offW, L::nW, tt * NKB + half * KBH + kk, lane); };
-        auto ldQ = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + half * KBH + kk, lane); };
+        auto ldW = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offW, L::nW, tt * NKB + part * KBH + kk, lane); };
+        auto ldQ = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + part * KBH + kk, lane); };
         Plain wf[4][KBH], qf[4][KBH];
         if (BF16) {
 #pragma unroll
@@ -776,35 +792,33 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
                 }
         }
         if (more) prefetch_u(c + 1, u_nx);
-        // this half's contribution to W S and Qh S
-        Split Sop[KBH];
+        // this part's contribution to W S and Qh S, one k-block at a time (the split of the next
+        // block's state rows can then issue while the products of this one run); every tile still
+        // sums its k-blocks in the same order
+        f32x4 wsa[4], qsa[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) { wsa[tt] = zero4(); qsa[tt] = zero4(); }
 #pragma unroll
         for (int kk = 0; kk < KBH; ++kk) {
             float vals[8] = {S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3],
                              S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
-            Sop[kk] = P::split(vals);
-        }
-        f32x4 wsa[4], qsa[4];
+            const Split sop = P::split(vals);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            wsa[tt] = zero4();
-            qsa[tt] = zero4();
-#pragma unroll
-            for (int kk = 0; kk < KBH; ++kk) {
-                wsa[tt] = mfma(BF16 ? wf[tt][kk] : ldW(tt, kk), Sop[kk], wsa[tt]);
-                qsa[tt] = mfma(BF16 ? qf[tt][kk] : ldQ(tt, kk), Sop[kk], qsa[tt]);
+            for (int tt = 0; tt < 4; ++tt) {
+                wsa[tt] = mfma(BF16 ? wf[tt][kk] : ldW(tt, kk), sop, wsa[tt]);
+                qsa[tt] = mfma(BF16 ? qf[tt][kk] : ldQ(tt, kk), sop, qsa[tt]);
             }
         }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) xws[ct][half][tt][lane] = wsa[tt];
-        // Qh S partials of the other half's output tiles ({1, 2} for half 0, {0, 3} for half 1)
-        xqs[ct][half][0][lane] = half ? qsa[0] : qsa[1];
-        xqs[ct][half][1][lane] = half ? qsa[3] : qsa[2];
+        for (int tt = 0; tt < 4; ++tt) {
+            xws[ct][part][tt][lane] = wsa[tt];
+            if (!owns(part, tt)) xqs[ct][part][qslot(part, tt)][lane] = qsa[tt];
+        }
         // operands of the second part of the chunk, requested before the barrier
         // (with a producer the buffer is refilled right after the exchange barrier, so every
         // read of it must be issued before; without one, fp32 fragments are read next to use)
         constexpr bool kEarlyK = BF16 || kProd;
-        auto ldK = [&](int r, int kb2) __attribute__((always_inline)) { return P::ld_plain(sb + L::offK, L::nK, (half * RTH + r) * 2 + kb2, lane); };
+        auto ldK = [&](int r, int kb2) __attribute__((always_inline)) { return P::ld_plain(sb + L::offK, L::nK, (part * RTH + r) * 2 + kb2, lane); };
         Plain kf[RTH][2];
         if (kEarlyK) {
 #pragma unroll
@@ -812,25 +826,32 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
                 for (int kb2 = 0; kb2 < 2; ++kb2) kf[r][kb2] = ldK(r, kb2);
         }
-        const Split af0 = P::ld_split(sb + L::offA, L::nA, aidx(ot0, 0), lane);
-        const Split af10 = P::ld_split(sb + L::offA, L::nA, aidx(ot1, 0), lane);
-        const Split af11 = P::ld_split(sb + L::offA, L::nA, aidx(ot1, 1), lane);
+        // Aqk fragments of the own output tiles: one k-block for tiles 0 and 1, two for 2 and 3
+        Split af[NOT][2];
+#pragma unroll
+        for (int i = 0; i < NOT; ++i) {
+            const int ot = own_tile(i);
+            af[i][0] = P::ld_split(sb + L::offA, L::nA, aidx(ot, 0), lane);
+            af[i][1] = P::ld_split(sb + L::offA, L::nA, aidx(ot, ot >= 2 ? 1 : 0), lane);
+        }
         f32x4 e_cur[RTH];
 #pragma unroll
         for (int r = 0; r < RTH; ++r)
-            e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (half * RTH + r) + 4 * grp));
+            e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (part * RTH + r) + 4 * grp));
         // rows of the previous chunk (left in obuf before the top barrier; refilled after the
         // exchange barrier)
         if (kProd && c > 0) store_rows(c - 1);
         // exchange barrier: only LDS traffic must be complete (lgkmcnt); copies into the other
         // stage buffer stay in flight (a fence here would wait for them too)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // Ud = U - (W S [half 0] + W S [half 1])
+        // Ud = U - (W S [part 0] + W S [part 1] + ...), every wave in the same order
         f32x4 ud[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-            const f32x4 oth = xws[ct][half ^ 1][tt][lane];
-            ud[tt] = u_cur[tt] - (half ? oth + wsa[tt] : wsa[tt] + oth);
+            f32x4 sum = xws[ct][0][tt][lane];
+#pragma unroll
+            for (int pp = 1; pp < NS; ++pp) sum += xws[ct][pp][tt][lane];
+            ud[tt] = u_cur[tt] - sum;
         }
         Split Uop[2];
 #pragma unroll
@@ -839,41 +860,43 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
                              ud[2 * kb2 + 1][0], ud[2 * kb2 + 1][1], ud[2 * kb2 + 1][2], ud[2 * kb2 + 1][3]};
             Uop[kb2] = P::split(vals);
         }
-        // O rows of tiles ot0 (one Aqk k-block) and ot1 (two)
-        f32x4 oo[2];
-        {
-            const f32x4 q0 = half ? qsa[1] : qsa[0], q1 = half ? qsa[2] : qsa[3];
-            const f32x4 p0 = xqs[ct][half ^ 1][0][lane], p1 = xqs[ct][half ^ 1][1][lane];
-            f32x4 oa0 = half ? p0 + q0 : q0 + p0;
-            f32x4 oa1 = half ? p1 + q1 : q1 + p1;
-            oa0 = mfma(af0, Uop[0], oa0);
-            oa1 = mfma(af10, Uop[0], oa1);
-            oa1 = mfma(af11, Uop[1], oa1);
-            oo[0] = oa0;
-            oo[1] = oa1;
+        // O rows of the own tiles (Qh S summed over the parts in part order, then Aqk Ud) and
+        // the state update; the products that need only the first k-block of Ud come first
+        f32x4 oo[NOT], Sn[RTH];
+#pragma unroll
+        for (int i = 0; i < NOT; ++i) {
+            const int ot = own_tile(i);
+            const f32x4 mine = ot == 0 ? qsa[0] : ot == 1 ? qsa[1] : ot == 2 ? qsa[2] : qsa[3];
+            oo[i] = part == 0 ? mine : xqs[ct][0][qslot(0, ot)][lane];
+#pragma unroll
+            for (int pp = 1; pp < NS; ++pp) oo[i] += pp == part ? mine : xqs[ct][pp][qslot(pp, ot)][lane];
         }
 #pragma unroll
-        for (int r = 0; r < RTH; ++r) {
-            f32x4 acc = S[r] * e_cur[r];
+        for (int r = 0; r < RTH; ++r) Sn[r] = S[r] * e_cur[r];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2) acc = mfma(kEarlyK ? kf[r][kb2] : ldK(r, kb2), Uop[kb2], acc);
-            S[r] = acc;
-        }
+        for (int i = 0; i < NOT; ++i) oo[i] = mfma(af[i][0], Uop[0], oo[i]);
+#pragma unroll
+        for (int r = 0; r < RTH; ++r) Sn[r] = mfma(kEarlyK ? kf[r][0] : ldK(r, 0), Uop[0], Sn[r]);
+#pragma unroll
+        for (int i = 0; i < NOT; ++i)
+            if (own_tile(i) >= 2) oo[i] = mfma(af[i][1], Uop[1], oo[i]);
+#pragma unroll
+        for (int r = 0; r < RTH; ++r) S[r] = mfma(kEarlyK ? kf[r][1] : ldK(r, 1), Uop[1], Sn[r]);
         if (kProd) {
             // rows of this chunk (the previous ones were read before the exchange barrier)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NOT; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    IO<TIO>::store(&obuf[16 * (i ? ot1 : ot0) + 4 * grp + e][0], ct * 16 + r16, scale * oo[i][e]);
+                    IO<TIO>::store(&obuf[16 * own_tile(i) + 4 * grp + e][0], ct * 16 + r16, scale * oo[i][e]);
         } else {
             const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
             TIO *ob = o + ((s_tok + c * kChunk) * H + h) * (long)D + col;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < NOT; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * (i ? ot1 : ot0) + 4 * grp + e;
+                    const int t = 16 * own_tile(i) + 4 * grp + e;
                     if (t < Cc) IO<TIO>::store(ob, (long)t * HD, scale * oo[i][e]);
                 }
             if (more) {
@@ -895,7 +918,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         for (int r = 0; r < RTH; ++r)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sN[sbase + (long)(16 * (half * RTH + r) + 4 * grp + e) * D + col] = S[r][e];
+                sN[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] = S[r][e];
     }
 }
 
@@ -921,11 +944,12 @@ static hipError_t launch_local_t(const FwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <bool BF16, int D, int NCT>
+template <bool BF16, int D, int NCT, int NS>
 static hipError_t launch_scan_nct(const FwdArgs &a, hipStream_t st, int nchains) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NCT);
-    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT>), dim3((unsigned)blocks), dim3(scan_threads<BF16, D, NCT>()), 0, st,
+    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT, NS>), dim3((unsigned)blocks),
+                       dim3(scan_threads<BF16, D, NCT, NS>()), 0, st,
                        a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale, a.s0, a.sN, (TIO *)a.o, (const char *)a.ws);
     return hipGetLastError();
 }
@@ -946,15 +970,18 @@ static int device_cu_count() {
 }
 
 // Column tiles per workgroup: two when that still gives every CU a workgroup (the tiles then
-// share one LDS copy of the chunk's operands), else one.
+// share one LDS copy of the chunk's operands), else one with the state split over more waves.
 template <bool BF16, int D>
 static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
     const int nchains = a.N * a.H;
     if (nchains <= 0) return hipSuccess;
     const int cus = device_cu_count();
     const long tiles = (long)nchains * (D / 16);
-    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2>(a, st, nchains);
-    return launch_scan_nct<BF16, D, 1>(a, st, nchains);
+    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2, 2>(a, st, nchains);
+    // too few tiles to give every CU a two-tile workgroup: one tile per workgroup, and at
+    // d = 128 four waves per tile (a shorter serial chain per chunk)
+    if constexpr (D == 128) return launch_scan_nct<BF16, D, 1, 4>(a, st, nchains);
+    else return launch_scan_nct<BF16, D, 1, 2>(a, st, nchains);
 }
 
 hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {
