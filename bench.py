@@ -7,12 +7,13 @@ The same run also measures
     100 consecutive steps): state GB/s and fraction of HBM peak;
   * the q/k prologue on the packed 64-sequence batch (lengths U[512, 16384], H = 32):
     GB/s;
+  * the prefill batch with one decay per token and head, and with none (kda_fwd_scalar_gate);
   * the long-context prefill (B = 1, H = 32, T = 131072) and the varlen layer (prologue on q
     and k, then the prefill of the packed 64-sequence batch): ms and tokens/s;
   * the fp64 CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel times come from HIP events recorded on the stream the kernels run on.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,long,varlen,cpu,copy]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,scalar,long,varlen,cpu,copy]
 Prints one JSON line.  `--only copy` runs a plain 256 MiB device copy (a kernel of known size
 used to calibrate the FETCH_SIZE / WRITE_SIZE counters of profiler runs).
 The roofline "traffic" figure comes from profiles/traffic.json (counter runs of this same
@@ -232,6 +233,40 @@ def bench_long(torch, kda, dev, reps=5):
             "hbm_frac": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * th / ms / 1e6 / HBM_PEAK_GBS}
 
 
+def bench_scalar_gate(torch, kda, dev, reps=20):
+    """The prefill batch (B=4, H=16, T=4096, d=128, bf16) with one log-decay per token and head
+    (kda_fwd_scalar_gate), and with none (alpha = 1)."""
+    B, T, H, d = 4, 4096, 16, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93106)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    q, k = _unit_bf16(rnd(B, T, H, d)), _unit_bf16(rnd(B, T, H, d))
+    v = rnd(B, T, H, d).to(torch.bfloat16)
+    beta = torch.sigmoid(rnd(B, T, H))
+    g = -torch.nn.functional.softplus(rnd(B, T, H) + 2)
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = kda.fwd_workspace_bytes(kda.KDA_BF16, B, T, H, d, d, B, False)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    L = kda.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: None if t is None else t.data_ptr()
+
+    def run(gp):
+        assert L.kda_fwd_scalar_gate(kda.KDA_BF16, B, T, H, d, d, None, B, p(q), p(k), p(v), gp, p(beta), 1.0,
+                                     None, p(S), p(o), p(ws), nws, st) == 0
+
+    out = {"workload": "KDA prefill B=4 H=16 T=4096 d=128 bf16, one log-decay per token and head "
+                       "(Gated DeltaNet case) and alpha = 1 (DeltaNet case)"}
+    for label, gp in (("per_head_decay", p(g)), ("alpha_one", None)):
+        for _ in range(3):
+            run(gp)
+        torch.cuda.synchronize()
+        ms = time_events(lambda: run(gp), reps, torch)
+        out[label] = {"ms": ms, "tokens_per_s": B * T / (ms / 1e3)}
+    return out
+
+
 def bench_varlen_layer(torch, kda, dev, reps=5):
     """Varlen layer: 64 packed sequences (lengths U[512, 16384] from the workload seed), H=32, d=128:
     prologue on raw q and k (width 4), then the chunked prefill with per-sequence S_0 ~ N(0, 0.02)."""
@@ -339,8 +374,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,prep,long,varlen,cpu",
-                    help="comma list of prefill, decode, prep, long, varlen, cpu, copy")
+    ap.add_argument("--only", default="prefill,decode,prep,scalar,long,varlen,cpu",
+                    help="comma list of prefill, decode, prep, scalar, long, varlen, cpu, copy")
     args = ap.parse_args()
     only = set(x.strip() for x in args.only.split(",") if x.strip())
     if args.gpus != 1:
@@ -358,6 +393,12 @@ def main():
             out["decode"] = bench_decode(args, torch, kda, dev)
         if "prep" in only:
             out["prep"] = bench_prep(args, torch, kda, dev)
+        if "scalar" in only:
+            out["scalar_gate"] = bench_scalar_gate(torch, kda, dev)
+        if "long" in only:
+            out["long_context"] = bench_long(torch, kda, dev)
+        if "varlen" in only:
+            out["varlen_layer"] = bench_varlen_layer(torch, kda, dev)
         if "copy" in only:
             out["copy"] = bench_copy(torch, dev)
         print(json.dumps(out), flush=True)
@@ -414,6 +455,9 @@ def main():
         pr = bench_prep(args, torch, kda, dev)
         out["prep"] = {"workload": f"{pr['tokens']} packed tokens (64 sequences), H=32, d=128, width 4, bf16",
                        "ms": pr["ms"], "GBs": pr["gbs"], "frac": pr["gbs"] / HBM_PEAK_GBS}
+    if "scalar" in only:
+        log("scalar gate ...")
+        out["scalar_gate"] = bench_scalar_gate(torch, kda, dev)
     if "long" in only:
         log("long context ...")
         out["long_context"] = bench_long(torch, kda, dev)

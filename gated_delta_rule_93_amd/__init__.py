@@ -5,6 +5,7 @@ PyTorch supplies device memory and the current stream.  There is no CPU fallback
 library is missing, importing works but the first call raises.
 
     o, S = fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None)
+    o, S = fwd_scalar_gate(q, k, v, g_or_None, beta, ...)    # g [B, T, H]: one decay per head
     o    = decode_step(q, k, v, g, beta, state, scale=1.0)     # state updated in place
     y    = prep(x, conv_w, cu_seqlens=None)
 
@@ -48,6 +49,8 @@ def lib():
         L.kda_fwd_workspace_bytes.restype = S
         L.kda_fwd.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, F, P, P, P, P, S, P]
         L.kda_fwd.restype = I
+        L.kda_fwd_scalar_gate.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, F, P, P, P, P, S, P]
+        L.kda_fwd_scalar_gate.restype = I
         L.kda_fwd_chunk_local.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, P, S, P]
         L.kda_fwd_chunk_local.restype = I
         L.kda_fwd_state_scan.argtypes = [I, I, I, I, I, I, P, I, F, P, P, P, P, S, P]
@@ -116,6 +119,21 @@ def fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=Non
         output_final_state: bool = True, o=None, final_state=None, workspace=None,
         stream=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunked prefill (kda_fwd).  Returns (o, final_state or None)."""
+    return _fwd(False, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
+                final_state, workspace, stream)
+
+
+def fwd_scalar_gate(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=None,
+                    output_final_state: bool = True, o=None, final_state=None, workspace=None,
+                    stream=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Chunked prefill with one log-decay per token and head, g [B, T, H], or g = None for
+    alpha = 1 (kda_fwd_scalar_gate).  Returns (o, final_state or None)."""
+    return _fwd(True, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
+                final_state, workspace, stream)
+
+
+def _fwd(scalar_gate, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
+         final_state, workspace, stream):
     torch = _torch()
     io = _io_dtype(q)
     B, T, H, dk = q.shape
@@ -124,7 +142,11 @@ def fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=Non
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (B, T, H, dk))
     _need(v, "v", q.dtype, (B, T, H, dv))
-    _need(g, "g", torch.float32, (B, T, H, dk))
+    if scalar_gate:
+        if g is not None:
+            _need(g, "g", torch.float32, (B, T, H))
+    else:
+        _need(g, "g", torch.float32, (B, T, H, dk))
     _need(beta, "beta", torch.float32, (B, T, H))
     if initial_state is not None:
         _need(initial_state, "initial_state", torch.float32, (N, H, dk, dv))
@@ -141,10 +163,11 @@ def fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=Non
     need = fwd_workspace_bytes(io, B, T, H, dk, dv, N, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().kda_fwd(io, B, T, H, dk, dv, _ptr(cu_seqlens), N,
-                         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
-                         _ptr(initial_state), _ptr(final_state), _ptr(o),
-                         _ptr(workspace), workspace.numel(), _stream(stream)))
+    fn = lib().kda_fwd_scalar_gate if scalar_gate else lib().kda_fwd
+    _check(fn(io, B, T, H, dk, dv, _ptr(cu_seqlens), N,
+              _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+              _ptr(initial_state), _ptr(final_state), _ptr(o),
+              _ptr(workspace), workspace.numel(), _stream(stream)))
     return o, final_state
 
 

@@ -43,7 +43,7 @@ enum FwdPart { kLocal = 1, kScan = 2, kBoth = 3 };
 kda_status_t check_fwd(int part, kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
                        const int32_t *cu_seqlens, int N, const void *q, const void *k, const void *v,
                        const float *g, const float *beta, const float *s0, const float *sN, const void *o,
-                       const void *workspace, size_t workspace_bytes) {
+                       const void *workspace, size_t workspace_bytes, bool g_optional = false) {
     if (!valid_dtype(io) || B < 0 || T < 0 || H < 0 || N < 0 || d_k <= 0 || d_v <= 0)
         return KDA_ERR_INVALID_ARGUMENT;
     if (cu_seqlens) {
@@ -56,8 +56,9 @@ kda_status_t check_fwd(int part, kda_dtype_t io, int B, int T, int H, int d_k, i
     const long tokens = (long)B * T;
     if (tokens > 0 && H > 0) {
         if (part & kLocal) {
-            if (!q || !k || !v || !g || !beta) return KDA_ERR_INVALID_ARGUMENT;
-            if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g)) return KDA_ERR_INVALID_ARGUMENT;
+            if (!q || !k || !v || (!g && !g_optional) || !beta) return KDA_ERR_INVALID_ARGUMENT;
+            if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (g && !aligned16(g)))
+                return KDA_ERR_INVALID_ARGUMENT;
         }
         if (part & kScan) {
             if (!o || !aligned16(o)) return KDA_ERR_INVALID_ARGUMENT;
@@ -76,7 +77,7 @@ kda::FwdArgs fwd_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, con
     a.bf16 = io == KDA_BF16;
     a.B = B; a.T = T; a.H = H; a.dk = d_k; a.dv = d_v; a.N = N;
     a.cu_seqlens = cu_seqlens;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.scale = scale;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.scalar_gate = false; a.scale = scale;
     a.s0 = s0; a.sN = sN; a.o = o; a.ws = workspace;
     return a;
 }
@@ -94,6 +95,19 @@ kda_status_t kda_fwd(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, cons
     if (st != KDA_OK || (long)N * H == 0) return st;
     const kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, scale, initial_state,
                                     final_state, o, workspace);
+    return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_fwd_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,
+                                 int N, const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, float scale, const float *initial_state, float *final_state,
+                                 void *o, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    kda_status_t st = check_fwd(kBoth, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, initial_state,
+                                final_state, o, workspace, workspace_bytes, true);
+    if (st != KDA_OK || (long)N * H == 0) return st;
+    kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, scale, initial_state,
+                              final_state, o, workspace);
+    a.scalar_gate = true;
     return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 

@@ -208,6 +208,147 @@ template <> struct Raw4<float> {
     __device__ __forceinline__ float elem(int u) const { return w[u]; }
 };
 
+// Phases shared by the chunk-local kernels once Akk (beta applied, strictly lower) and Aqk
+// (lower, incl. the diagonal) are in LDS: the UT transform Tm = (I + Akk)^-1, the Aqk
+// fragments, V^T, and W = T' X, U = T' V.  `vv` holds this thread's V rows (layout of the load
+// phase: rows rg*RPG.., channels c4..c4+3); `Xf` the X^T = (K e^G)^T fragments of k-block `wave`.
+template <bool BF16, int D, int RPG, typename SM>
+__device__ __forceinline__ void ut_and_outputs(SM &sm, const Raw4<typename SM::TIO> (&vv)[RPG],
+                                               const typename Prec<BF16>::Plain (&Xf)[2][2], char *wsb, int rg,
+                                               int c4) {
+    using TIO = typename SM::TIO;
+    using P = Prec<BF16>;
+    using L = WsLayout<BF16, D>;
+    using Plain = typename P::Plain;
+    using Split = typename P::Split;
+    constexpr int NKB = L::NKB, NRT = L::NRT;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    char *wsW = wsb + L::offW, *wsA = wsb + L::offA;
+    float *wsU = reinterpret_cast<float *>(wsb + L::offU);
+    // ---------------- phase 4: Tm = (I + Akk)^-1 (unit lower triangular), fp32
+    if (wave == 0) {  // 16x16 diagonal blocks: lane owns column j of block b
+        const int b = lane >> 4, j = lane & 15;
+        float tc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc += sm.kq.a.Akk[16 * b + i][16 * b + m] * tc[m];
+            tc[i] = i == j ? 1.f : (i < j ? 0.f : -acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.g.T[16 * b + i][16 * b + j] = tc[i];
+    }
+    __syncthreads();
+    for (int I = 1; I < 4; ++I) {  // block rows: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
+        const int J = wave;
+        if (J < I) {
+            f32x4 x = zero4();
+            for (int M = J; M < I; ++M) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.kq.a.Akk[16 * I + r16][16 * M + 4 * grp + s],
+                                                             sm.g.T[16 * M + 4 * grp + s][16 * J + r16], x, 0, 0, 0);
+            }
+            f32x4 y = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.g.T[16 * I + r16][16 * I + 4 * grp + s], x[s], y, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.g.T[16 * I + 4 * grp + e][16 * J + r16] = -y[e];
+        }
+        __syncthreads();
+    }
+
+    // ---------------- phase 5: Aqk fragments; then V^T into the dead Akk/Aqk region;
+    // W = T' X and U = T' V.
+    for (int f = wave; f < 6; f += 4) {  // Aqk fragments
+        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
+        const int t = 16 * tt + r16;
+        float vals[8];
+        ld_kslots(&sm.kq.a.Aqk[t][0], kb2, grp, vals);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)  // causal mask, incl. the diagonal (entries above were never written)
+            if (32 * kb2 + kslot(grp, s) > t) vals[s] = 0.f;
+        P::st_split(wsA, L::nA, f, lane, P::split(vals));
+    }
+    __syncthreads();  // Akk, Aqk are dead from here on
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // channel c4 + u: RPG consecutive tokens, one vector store
+        union { TIO e[RPG]; uint4 q[(RPG * sizeof(TIO) + 15) / 16]; uint2 d; } col;
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) col.e[r] = vv[r].elem(u);
+        TIO *dst = &sm.kq.VT[c4 + u][rg * RPG];
+        if constexpr (RPG * sizeof(TIO) == 8) {
+            *reinterpret_cast<uint2 *>(dst) = col.d;
+        } else {
+#pragma unroll
+            for (int w = 0; w < (int)(RPG * sizeof(TIO) / 16); ++w) reinterpret_cast<uint4 *>(dst)[w] = col.q[w];
+        }
+    }
+    __syncthreads();
+    // T' = Tm Diag(beta) fragments; the same values serve as the A operand (row t, k = t')
+    // of U and as the B operand (k = t', column t) of W^T.
+    Split Tf[6];
+#pragma unroll
+    for (int f = 0; f < 6; ++f) {
+        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
+        float vals[8], bv[8];
+        ld_kslots(&sm.g.T[16 * tt + r16][0], kb2, grp, vals);
+        ld_kslots(&sm.beta[0], kb2, grp, bv);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)  // Tm is zero above its 16x16 diagonal blocks (never written)
+            vals[s] = ((32 * kb2 + kslot(grp, s)) >> 4) <= tt ? vals[s] * bv[s] : 0.f;
+        Tf[f] = P::split(vals);
+    }
+    for (int kb = wave; kb < NKB; kb += 4) {  // W fragments (tt, kb)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+                for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc[r2] = mfma(Xf[r2][kb2], Tf[aidx(tt, kb2)], acc[r2]);
+            float vals[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+            P::st_plain(wsW, L::nW, tt * NKB + kb, lane, P::plain(vals));
+        }
+    }
+    for (int jt = wave; jt < NRT; jt += 4) {  // U tiles (jt, tt)
+        Plain Vf[2];
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            float vals[8];
+            ld_kslots(&sm.kq.VT[16 * jt + r16][0], kb2, grp, vals);
+            Vf[kb2] = P::plain(vals);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc = mfma(Tf[aidx(tt, kb2)], Vf[kb2], acc);
+            reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
+        }
+    }
+}
+
+// (chunk slot, head) of chunk-local workgroup `id`.  The 1-D grid runs in reverse consumption
+// order: the chunks the state scan reads first are written last, so they are the most likely
+// to still be in the memory-side cache.
+__device__ __forceinline__ void local_slot(long id, const int32_t *cu, int N, int T, int H, long nslots,
+                                           long &slot, int &h) {
+    if (cu) {
+        slot = nslots - 1 - id / H;
+        h = (int)(id % H);
+    } else {
+        const int ncs = (T + kChunk - 1) / kChunk;
+        const long per_c = (long)N * H;
+        const int c = ncs - 1 - (int)(id / per_c);
+        const long rem = id % per_c;
+        h = (int)(rem % H);
+        slot = (rem / H) * ncs + c;
+    }
+}
+
 template <bool BF16, int D>
 __global__ void __launch_bounds__(256, 2)
 chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
@@ -223,22 +364,9 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     constexpr int NKB = L::NKB, NRT = L::NRT;
     __shared__ ChunkSmem<BF16, D> sm;
 
-    // 1-D grid in reverse consumption order: the chunks the state scan reads first are written
-    // last, so they are the most likely to still be in the memory-side cache.
     long slot;
     int h;
-    const long id = blockIdx.x;
-    if (cu) {
-        slot = nslots - 1 - id / H;
-        h = (int)(id % H);
-    } else {
-        const int ncs = (T + kChunk - 1) / kChunk;
-        const long per_c = (long)N * H;
-        const int c = ncs - 1 - (int)(id / per_c);
-        const long rem = id % per_c;
-        h = (int)(rem % H);
-        slot = (rem / H) * ncs + c;
-    }
+    local_slot(blockIdx.x, cu, N, T, H, nslots, slot, h);
     const ChunkPos pos = locate_chunk(slot, cu, N, T);
     if (!pos.valid) return;  // uniform over the block
     const int Cc = pos.Cc;
@@ -297,8 +425,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     __syncthreads();
 
     // ---------------- phase 2: element-wise products, written as operand fragments
-    char *wsW = wsb + L::offW, *wsQ = wsb + L::offQ, *wsK = wsb + L::offK, *wsA = wsb + L::offA;
-    float *wsU = reinterpret_cast<float *>(wsb + L::offU);
+    char *wsQ = wsb + L::offQ, *wsK = wsb + L::offK;
     float *wsE = reinterpret_cast<float *>(wsb + L::offE);
     if (tid < D) wsE[tid] = fast_exp2(sm.g.G[kChunk - 1][tid]);
     for (int e = tid; e < 6 * D; e += 256) {
@@ -478,110 +605,182 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
         __syncthreads();
     }
 
-    // ---------------- phase 4: Tm = (I + Akk)^-1 (unit lower triangular), fp32
-    if (wave == 0) {  // 16x16 diagonal blocks: lane owns column j of block b
-        const int b = lane >> 4, j = lane & 15;
-        float tc[16];
+    ut_and_outputs<BF16, D, RPG>(sm, vv, Xf, wsb, rg, c4);
+}
+
+// ------------------------------------------------------------------ kernel 1s: chunk-local, one decay per token
+// Chunk-local kernel for a decay shared by all channels of a head: one log-decay per token and
+// head (the Gated DeltaNet special case of the operator), or none (alpha = 1: DeltaNet).  The
+// factor e^{G_i - G_j} of the decayed Gram matrices then leaves the channel sum, so Akk and Aqk
+// are the plain products K K^T and Q K^T (bf16 inputs: exact products, fp32 sums) scaled
+// element-wise, with no per-channel exponentials.  The record it writes is the one of the
+// per-channel kernel (e^gamma repeated over the channels), read by the same state scan.
+template <bool BF16, int D> struct alignas(16) ChunkSmemS {
+    using TIO = typename std::conditional<BF16, uint16_t, float>::type;
+    static constexpr int KS = D + 8, VS = kChunk + 8, AS = kChunk + 4;
+    static constexpr int CQ = D / 4;          // channel quads
+    static constexpr int RG = 256 / CQ;       // row groups in the load layout
+    static constexpr int RPG = kChunk / RG;   // rows per group
+    union {
+        float T[kChunk][AS];  // the UT transform Tm
+    } g;
+    union {
+        struct { TIO K[kChunk][KS]; TIO Q[kChunk][KS]; } in;
+        struct { float Akk[kChunk][AS]; float Aqk[kChunk][AS]; } a;
+        TIO VT[D][VS];
+    } kq;
+    float G[kChunk];    // cumulative log2-decay of each token
+    float eG[kChunk];   // 2^G
+    float eGm[kChunk];  // 2^(gamma - G)
+    float beta[kChunk];
+};
+
+template <bool BF16, int D>
+__global__ void __launch_bounds__(256, (BF16 ? 3 : 1))  // bf16: 53 KB LDS, three workgroups per CU
+chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ q,
+                          const typename ChunkSmemS<BF16, D>::TIO *__restrict__ k,
+                          const typename ChunkSmemS<BF16, D>::TIO *__restrict__ v,
+                          const float *__restrict__ g, const float *__restrict__ beta,
+                          const int32_t *__restrict__ cu, int N, int T, int H, long nslots, char *__restrict__ ws) {
+    using SM = ChunkSmemS<BF16, D>;
+    using TIO = typename SM::TIO;
+    using P = Prec<BF16>;
+    using L = WsLayout<BF16, D>;
+    using Plain = typename P::Plain;
+    constexpr int NKB = L::NKB;
+    constexpr int RPG = SM::RPG;
+    __shared__ SM sm;
+
+    long slot;
+    int h;
+    local_slot(blockIdx.x, cu, N, T, H, nslots, slot, h);
+    const ChunkPos pos = locate_chunk(slot, cu, N, T);
+    if (!pos.valid) return;  // uniform over the block
+    const int Cc = pos.Cc;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    char *wsb = ws + ((size_t)slot * H + h) * L::bytes;
+    const long rowstride = (long)H * D;
+    const long base_in = (pos.tok0 * H + h) * (long)D;
+
+    // ---------------- phase 1: loads (rows >= Cc are zero); per-token cumulative log2-decay
+    const int rg = tid / SM::CQ, c4 = (tid % SM::CQ) * 4;
+    Raw4<TIO> kv[RPG], qv[RPG], vv[RPG];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = 0.f;
+    for (int r = 0; r < RPG; ++r) {
+        const int t = rg * RPG + r;
+        const long off = base_in + (t < Cc ? t : 0) * rowstride + c4;
+        kv[r] = Raw4<TIO>::load(k + off);
+        qv[r] = Raw4<TIO>::load(q + off);
+        vv[r] = Raw4<TIO>::load(v + off);
+    }
+    if (wave == 0) {  // lane t: token t of the chunk
+        const long tp = (pos.tok0 + (lane < Cc ? lane : 0)) * H + h;
+        const float braw = beta[tp];
+        float gl = g ? g[tp] * kLog2e : 0.f;
+        if (lane >= Cc) gl = 0.f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) acc += sm.kq.a.Akk[16 * b + i][16 * b + m] * tc[m];
-            tc[i] = i == j ? 1.f : (i < j ? 0.f : -acc);
+        for (int off = 1; off < 64; off <<= 1) {  // inclusive prefix sum over the 64 lanes
+            const float y = __shfl_up(gl, off);
+            if (lane >= off) gl += y;
         }
+        const float gam = __shfl(gl, 63);
+        sm.G[lane] = gl;
+        sm.eG[lane] = fast_exp2(gl);
+        sm.eGm[lane] = fast_exp2(gam - gl);
+        sm.beta[lane] = lane < Cc ? braw : 0.f;
+    }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.g.T[16 * b + i][16 * b + j] = tc[i];
+    for (int r = 0; r < RPG; ++r) {
+        const int t = rg * RPG + r;
+        if (t >= Cc) {
+            kv[r] = Raw4<TIO>::zero();
+            qv[r] = Raw4<TIO>::zero();
+            vv[r] = Raw4<TIO>::zero();
+        }
+        kv[r].store(&sm.kq.in.K[t][c4]);
+        qv[r].store(&sm.kq.in.Q[t][c4]);
     }
     __syncthreads();
-    for (int I = 1; I < 4; ++I) {  // block rows: T_IJ = -T_II sum_{M=J}^{I-1} A_IM T_MJ
-        const int J = wave;
-        if (J < I) {
-            f32x4 x = zero4();
-            for (int M = J; M < I; ++M) {
+
+    // ---------------- phase 2: Qh = Q e^G, Kh^T = (K e^{gamma - G})^T, X^T = (K e^G)^T
+    char *wsQ = wsb + L::offQ, *wsK = wsb + L::offK;
+    float *wsE = reinterpret_cast<float *>(wsb + L::offE);
+    if (tid < D) wsE[tid] = sm.eG[kChunk - 1];  // e^gamma, the same for every channel
+    Plain Xf[2][2];
+    for (int kb = wave; kb < NKB; kb += 4) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.kq.a.Akk[16 * I + r16][16 * M + 4 * grp + s],
-                                                             sm.g.T[16 * M + 4 * grp + s][16 * J + r16], x, 0, 0, 0);
-            }
-            f32x4 y = zero4();
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = 16 * tt + r16;
+            float vals[8];
+            ld_kslots(&sm.kq.in.Q[t][0], kb, grp, vals);
+            const float f = sm.eG[t];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                y = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.g.T[16 * I + r16][16 * I + 4 * grp + s], x[s], y, 0, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.g.T[16 * I + 4 * grp + e][16 * J + r16] = -y[e];
+            for (int s = 0; s < 8; ++s) vals[s] *= f;
+            P::st_plain(wsQ, L::nQ, tt * NKB + kb, lane, P::plain(vals));
         }
-        __syncthreads();
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int rt = 2 * kb + r2, i = 16 * rt + r16;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                float eg[8], egm[8], kh[8], xv[8];
+                ld_kslots(&sm.eG[0], kb2, grp, eg);
+                ld_kslots(&sm.eGm[0], kb2, grp, egm);
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const float kvv = IO<TIO>::load(&sm.kq.in.K[32 * kb2 + kslot(grp, s)][0], i);
+                    kh[s] = kvv * egm[s];
+                    xv[s] = kvv * eg[s];
+                }
+                P::st_plain(wsK, L::nK, rt * 2 + kb2, lane, P::plain(kh));
+                Xf[r2][kb2] = P::plain(xv);
+            }
+        }
     }
 
-    // ---------------- phase 5: Aqk fragments; then V^T into the dead Akk/Aqk region;
-    // W = T' X and U = T' V.
-    for (int f = wave; f < 6; f += 4) {  // Aqk fragments
-        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
-        const int t = 16 * tt + r16;
-        float vals[8];
-        ld_kslots(&sm.kq.a.Aqk[t][0], kb2, grp, vals);
+    // ---------------- phase 3: Akk = beta_i e^{G_i - G_j} k_i.k_j (j < i), Aqk = e^{G_i - G_j} q_i.k_j (j <= i)
+    // The ten lower 16x16 tile pairs are dealt to the waves (pairs w, w + 4, w + 8); each wave sums
+    // all channels of its pairs, so no reduction between waves is needed.
+    f32x4 accK[3], accQ[3];
 #pragma unroll
-        for (int s = 0; s < 8; ++s)  // causal mask, incl. the diagonal (entries above were never written)
-            if (32 * kb2 + kslot(grp, s) > t) vals[s] = 0.f;
-        P::st_split(wsA, L::nA, f, lane, P::split(vals));
+    for (int u = 0; u < 3; ++u) {
+        accK[u] = zero4();
+        accQ[u] = zero4();
+        const int p = wave + 4 * u;
+        if (p < 10) {
+            int I, J;
+            pair_ij(p, I, J);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                float ka[8], qa[8], kbv[8];
+                ld_kslots(&sm.kq.in.K[16 * I + r16][0], kb, grp, ka);
+                ld_kslots(&sm.kq.in.Q[16 * I + r16][0], kb, grp, qa);
+                ld_kslots(&sm.kq.in.K[16 * J + r16][0], kb, grp, kbv);
+                const Plain bop = P::plain(kbv);
+                accK[u] = mfma(P::plain(ka), bop, accK[u]);
+                accQ[u] = mfma(P::plain(qa), bop, accQ[u]);
+            }
+        }
     }
-    __syncthreads();  // Akk, Aqk are dead from here on
+    __syncthreads();  // every wave is done reading K, Q (aliased by Akk, Aqk below)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {  // channel c4 + u: RPG consecutive tokens, one vector store
-        union { TIO e[RPG]; uint4 q[(RPG * sizeof(TIO) + 15) / 16]; uint2 d; } col;
+    for (int u = 0; u < 3; ++u) {
+        const int p = wave + 4 * u;
+        if (p < 10) {
+            int I, J;
+            pair_ij(p, I, J);
 #pragma unroll
-        for (int r = 0; r < RPG; ++r) col.e[r] = vv[r].elem(u);
-        TIO *dst = &sm.kq.VT[c4 + u][rg * RPG];
-        if constexpr (RPG * sizeof(TIO) == 8) {
-            *reinterpret_cast<uint2 *>(dst) = col.d;
-        } else {
-#pragma unroll
-            for (int w = 0; w < (int)(RPG * sizeof(TIO) / 16); ++w) reinterpret_cast<uint4 *>(dst)[w] = col.q[w];
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * I + 4 * grp + e, col = 16 * J + r16;
+                const float dec = col <= row ? fast_exp2(sm.G[row] - sm.G[col]) : 0.f;  // <= 1
+                sm.kq.a.Akk[row][col] = col < row ? accK[u][e] * dec * sm.beta[row] : 0.f;
+                sm.kq.a.Aqk[row][col] = accQ[u][e] * dec;
+            }
         }
     }
     __syncthreads();
-    // T' = Tm Diag(beta) fragments; the same values serve as the A operand (row t, k = t')
-    // of U and as the B operand (k = t', column t) of W^T.
-    Split Tf[6];
-#pragma unroll
-    for (int f = 0; f < 6; ++f) {
-        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
-        float vals[8], bv[8];
-        ld_kslots(&sm.g.T[16 * tt + r16][0], kb2, grp, vals);
-        ld_kslots(&sm.beta[0], kb2, grp, bv);
-#pragma unroll
-        for (int s = 0; s < 8; ++s)  // Tm is zero above its 16x16 diagonal blocks (never written)
-            vals[s] = ((32 * kb2 + kslot(grp, s)) >> 4) <= tt ? vals[s] * bv[s] : 0.f;
-        Tf[f] = P::split(vals);
-    }
-    for (int kb = wave; kb < NKB; kb += 4) {  // W fragments (tt, kb)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 acc[2] = {zero4(), zero4()};
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2)
-#pragma unroll
-                for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc[r2] = mfma(Xf[r2][kb2], Tf[aidx(tt, kb2)], acc[r2]);
-            float vals[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3], acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
-            P::st_plain(wsW, L::nW, tt * NKB + kb, lane, P::plain(vals));
-        }
-    }
-    for (int jt = wave; jt < NRT; jt += 4) {  // U tiles (jt, tt)
-        Plain Vf[2];
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            float vals[8];
-            ld_kslots(&sm.kq.VT[16 * jt + r16][0], kb2, grp, vals);
-            Vf[kb2] = P::plain(vals);
-        }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc = mfma(Tf[aidx(tt, kb2)], Vf[kb2], acc);
-            reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
-        }
-    }
+
+    ut_and_outputs<BF16, D, RPG>(sm, vv, Xf, wsb, rg, c4);
 }
 
 // ------------------------------------------------------------------ kernel 2: state scan
@@ -984,7 +1183,22 @@ static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
     else return launch_scan_nct<BF16, D, 1, 2>(a, st, nchains);
 }
 
+template <bool BF16, int D>
+static hipError_t launch_local_scalar_t(const FwdArgs &a, hipStream_t st) {
+    using TIO = typename ChunkSmemS<BF16, D>::TIO;
+    const long slots = fwd_chunk_slots(a.B, a.T, a.N, a.cu_seqlens != nullptr);
+    if (slots <= 0 || a.H <= 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_local_scalar_kernel<BF16, D>), dim3((unsigned)(slots * a.H)), dim3(256), 0, st,
+                       (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T,
+                       a.H, slots, static_cast<char *>(a.ws));
+    return hipGetLastError();
+}
+
 hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {
+    if (a.scalar_gate) {
+        if (a.bf16) return a.dk == 128 ? launch_local_scalar_t<true, 128>(a, st) : launch_local_scalar_t<true, 64>(a, st);
+        return a.dk == 128 ? launch_local_scalar_t<false, 128>(a, st) : launch_local_scalar_t<false, 64>(a, st);
+    }
     if (a.bf16) return a.dk == 128 ? launch_local_t<true, 128>(a, st) : launch_local_t<true, 64>(a, st);
     return a.dk == 128 ? launch_local_t<false, 128>(a, st) : launch_local_t<false, 64>(a, st);
 }

@@ -34,6 +34,7 @@ struct FwdArgs {
     const int32_t *cu_seqlens;  // NULL: dense
     const void *q, *k, *v;
     const float *g, *beta;
+    bool scalar_gate;           // g is [B, T, H] (one log-decay per token and head), or NULL (alpha = 1)
     float scale;
     const float *s0;
     float *sN;

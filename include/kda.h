@@ -115,6 +115,28 @@ kda_status_t kda_fwd_state_scan(kda_dtype_t io, int B, int T, int H, int d_k, in
                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * kda_fwd_scalar_gate -- kda_fwd for a forget gate shared by all key channels of a head:
+ * alpha_t = exp(g_t) * (1, ..., 1) with one g per token and head (the Gated DeltaNet case,
+ * blog post-114 chapter 3, where the gate is one scalar for all channels; chapter 4 contrasts
+ * it with the per-channel gate of KDA), or alpha_t = 1 (DeltaNet, chapter 3) when g is NULL.
+ * The recurrence is the operator's above with that alpha, decay first (the course page's
+ * section 3 order; the chapter's Gated DeltaNet listing reads the memory before the decay,
+ * which this library does not follow).  Equal to kda_fwd with g broadcast over d_k, and
+ * faster: the decay leaves the channel sums of the chunk's Gram matrices.
+ *
+ *   g     [B, T, H] fp32 (log alpha per token and head, finite, <= 0), or NULL (alpha = 1)
+ *   all other arguments, layouts, the workspace (kda_fwd_workspace_bytes) and the error
+ *   behaviour are those of kda_fwd.
+ */
+kda_status_t kda_fwd_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                 const int32_t *cu_seqlens, int N,
+                                 const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta, float scale,
+                                 const float *initial_state, float *final_state,
+                                 void *o, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
  * kda_decode_step -- one token of the recurrence for N independent sequences, in place.
  * The state stays resident in HBM; each call reads and rewrites it once
  * (the fixed-size state of the course page's section 2 makes each step O(1) in the

@@ -276,3 +276,54 @@ def config4_conv_weights(H: int = 32, d: int = 128, width: int = 4):
     wq = rng.standard_normal((H * d, width), dtype=np.float32) * np.float32(0.5)
     wk = rng.standard_normal((H * d, width), dtype=np.float32) * np.float32(0.5)
     return wq, wk
+
+
+def make_scalar_gate(lengths, H: int, d: int, io: str, seed: int, s0_std: Optional[float] = 0.02,
+                     g_shift: float = 2.0, dense_B: Optional[int] = None, with_gate: bool = True):
+    """Inputs for the one-decay-per-head case: like make_varlen / make_dense but g is [B, T, H]
+    (g = -softplus(N(0,1) + g_shift) per token and head), or None when with_gate is False.
+    Dense when dense_B is given (then lengths is [T]).  Draw order per sequence: q, k, v,
+    x_beta, x_alpha (one per token and head), S_0."""
+    if dense_B is not None:
+        T = int(lengths[0])
+        rng = np.random.default_rng(seed)
+        q = _unit_rows(rng.standard_normal((dense_B, T, H, d), dtype=np.float32))
+        k = _unit_rows(rng.standard_normal((dense_B, T, H, d), dtype=np.float32))
+        v = rng.standard_normal((dense_B, T, H, d), dtype=np.float32)
+        xb = rng.standard_normal((dense_B, T, H), dtype=np.float32)
+        xa = rng.standard_normal((dense_B, T, H), dtype=np.float32)
+        S0 = None if s0_std is None else rng.standard_normal((dense_B, H, d, d), dtype=np.float32) * np.float32(s0_std)
+        beta = _map_f32(_sigmoid, xb)
+        g = _map_f32(lambda a: -_softplus(a.astype(np.float64) + g_shift), xa) if with_gate else None
+        return KDAInputs(_store(q, io), _store(k, io), _store(v, io), g, beta, S0, None, io)
+    lengths = [int(x) for x in lengths]
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(lengths)
+    Ttot = int(cu[-1])
+    q = np.empty((1, Ttot, H, d), np.float32)
+    k = np.empty((1, Ttot, H, d), np.float32)
+    v = np.empty((1, Ttot, H, d), np.float32)
+    beta = np.empty((1, Ttot, H), np.float32)
+    g = np.empty((1, Ttot, H), np.float32) if with_gate else None
+    S0 = np.empty((len(lengths), H, d, d), np.float32) if s0_std is not None else None
+    for n, L in enumerate(lengths):
+        rng = np.random.default_rng([seed, n])
+        s, e = cu[n], cu[n + 1]
+        q[0, s:e] = _store(_unit_rows(rng.standard_normal((L, H, d), dtype=np.float32)), io)
+        k[0, s:e] = _store(_unit_rows(rng.standard_normal((L, H, d), dtype=np.float32)), io)
+        v[0, s:e] = _store(rng.standard_normal((L, H, d), dtype=np.float32), io)
+        beta[0, s:e] = _map_f32(_sigmoid, rng.standard_normal((L, H), dtype=np.float32))
+        xa = rng.standard_normal((L, H), dtype=np.float32)
+        if with_gate:
+            g[0, s:e] = _map_f32(lambda a: -_softplus(a.astype(np.float64) + g_shift), xa)
+        if S0 is not None:
+            S0[n] = rng.standard_normal((H, d, d), dtype=np.float32) * np.float32(s0_std)
+    return KDAInputs(q, k, v, g, beta, S0, cu.astype(np.int32), io)
+
+
+def broadcast_gate(g_scalar: Optional[np.ndarray], like: np.ndarray) -> np.ndarray:
+    """Per-channel log-decay array [..., H, d_k] equal to the per-head g on every channel (zeros for
+    g = None, i.e. alpha = 1)."""
+    if g_scalar is None:
+        return np.zeros(like.shape, np.float32)
+    return np.ascontiguousarray(np.broadcast_to(g_scalar[..., None], like.shape), dtype=np.float32)

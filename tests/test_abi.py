@@ -76,6 +76,33 @@ def test_fwd_rejects(over, code):
     assert fwd_call(**over) == code
 
 
+def scalar_call(**over):
+    a = dict(io=kda.KDA_BF16, B=1, T=64, H=1, dk=128, dv=128, cu=None, N=1, q=FAKE, k=FAKE, v=FAKE, g=FAKE,
+             beta=FAKE, scale=1.0, s0=None, sN=None, o=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return kda.lib().kda_fwd_scalar_gate(a["io"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["cu"], a["N"],
+                                         a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["s0"],
+                                         a["sN"], a["o"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(io=5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(beta=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(g=FAKE + 4), kda.KDA_ERR_INVALID_ARGUMENT),              # misaligned g
+    (dict(dk=96, dv=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(ws=None), kda.KDA_ERR_WORKSPACE),
+    (dict(g=None, ws=None), kda.KDA_ERR_WORKSPACE),                # g = NULL (alpha = 1) is valid
+])
+def test_fwd_scalar_gate_rejects(over, code):
+    assert scalar_call(**over) == code
+
+
+def test_per_channel_fwd_requires_g():
+    assert fwd_call(g=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert scalar_call(H=0, g=None, ws=None, wsb=0) == kda.KDA_OK
+
+
 def test_fwd_empty_problem_is_ok_without_launch():
     assert fwd_call(H=0, ws=None, wsb=0) == kda.KDA_OK
     assert fwd_call(B=0, N=0, T=0, ws=None, wsb=0) == kda.KDA_OK
