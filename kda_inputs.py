@@ -327,3 +327,67 @@ def broadcast_gate(g_scalar: Optional[np.ndarray], like: np.ndarray) -> np.ndarr
     if g_scalar is None:
         return np.zeros(like.shape, np.float32)
     return np.ascontiguousarray(np.broadcast_to(g_scalar[..., None], like.shape), dtype=np.float32)
+
+
+# --------------------------------------------------------------------------- low-rank gate inputs
+def gate_weights(Dm: int, H: int, d: int, r: int, seed: int, b_mean: float = 2.0, b_std: float = 0.5):
+    """Synthetic weights of the low-rank gate, bf16 values in fp32 storage except b (fp32):
+    w_down [r, Dm] and w_beta [H, Dm] ~ N(0, 1/Dm), w_up [H*d, r] ~ N(0, 1/r), b [H*d] ~ N(b_mean,
+    b_std).  With x ~ N(0, 1) both projections are then about N(0, 1), so the gate's pre-activation
+    is about N(b_mean, 1.1): the log-decay distribution of the other workloads (b_mean = 2), or a
+    weak decay (b_mean = -5).  Draw order: w_down, w_beta, w_up, b."""
+    rng = np.random.default_rng([seed, 1])
+    w_down = bf16_round(rng.standard_normal((r, Dm), dtype=np.float32) / np.float32(np.sqrt(Dm)))
+    w_beta = bf16_round(rng.standard_normal((H, Dm), dtype=np.float32) / np.float32(np.sqrt(Dm)))
+    w_up = bf16_round(rng.standard_normal((H * d, r), dtype=np.float32) / np.float32(np.sqrt(r)))
+    b = (np.float32(b_mean) + np.float32(b_std) * rng.standard_normal(H * d, dtype=np.float32)).astype(np.float32)
+    return w_down, w_beta, w_up, b
+
+
+def gate_hidden(Ntok: int, Dm: int, seed: int) -> np.ndarray:
+    """Hidden states x [Ntok, Dm] ~ N(0, 1), bf16 values in fp32 storage."""
+    rng = np.random.default_rng([seed, 2])
+    return _store_bf16_inplace(rng.standard_normal((Ntok, Dm), dtype=np.float32))
+
+
+@dataclasses.dataclass
+class LowRankInputs:
+    """Operator inputs with the gate given by its rank-r down projection z instead of g:
+    q, k, v [B, T, H, d] (bf16 values), beta [B, T, H], z [B, T, r] (bf16 values), w_up [H*d, r]
+    (bf16 values), b [H*d], S0 [N, H, d, d] or None, cu_seqlens or None."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    beta: np.ndarray
+    z: np.ndarray
+    w_up: np.ndarray
+    b: np.ndarray
+    S0: Optional[np.ndarray]
+    cu_seqlens: Optional[np.ndarray]
+
+    @property
+    def shape(self):
+        return self.q.shape
+
+
+def make_lowrank(B: int, T: int, H: int, d: int, r: int, seed: int, s0_std: Optional[float] = 0.02,
+                 b_mean: float = 2.0, lengths=None) -> LowRankInputs:
+    """bf16 inputs for the low-rank-gate forward.  Dense [B, T] when lengths is None, else packed
+    (B = 1, T = sum(lengths)).  Draw order: q, k, v, x_beta, z, S_0; then the gate weights from
+    gate_weights(seed) (w_up and b are used; w_down and w_beta belong to the prologue)."""
+    rng = np.random.default_rng(seed)
+    cu = None
+    if lengths is not None:
+        lengths = [int(x) for x in lengths]
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        B, T = 1, int(cu[-1])
+    q = _unit_rows(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    k = _unit_rows(rng.standard_normal((B, T, H, d), dtype=np.float32))
+    v = rng.standard_normal((B, T, H, d), dtype=np.float32)
+    beta = _map_f32(_sigmoid, rng.standard_normal((B, T, H), dtype=np.float32))
+    z = rng.standard_normal((B, T, r), dtype=np.float32)
+    N = B if cu is None else len(cu) - 1
+    S0 = None if s0_std is None else rng.standard_normal((N, H, d, d), dtype=np.float32) * np.float32(s0_std)
+    _, _, w_up, b = gate_weights(H * d, H, d, r, seed, b_mean=b_mean)
+    return LowRankInputs(bf16_round(q), bf16_round(k), bf16_round(v), beta, bf16_round(z), w_up, b, S0, cu)

@@ -8,6 +8,9 @@ Contents
   recurrence      token-by-token KDA recurrence in fp64 (C library `kda_oracle.c`,
                   one thread per independent (sequence, head) chain).
   prep            q/k prologue: short causal depthwise conv, SiLU, L2 norm (numpy fp64).
+  gate_z, gate_g, gate_beta, gate
+                  low-rank gate: z = x W_down^T, log(alpha) = -softplus(z W_up^T + b),
+                  beta = sigmoid(x w_beta^T) (numpy fp64).
 
 Sources (the pages this follows)
   * Course page "线性注意力与 KDA" (ai.air7.fun, Day 19), section 3: the decay
@@ -17,14 +20,19 @@ Sources (the pages this follows)
     vector over the key channels; q and k pass a short causal convolution and
     are L2-normalised.
   * Blog post ciyuanerhao.com post-114, chapter 3 (DeltaNet code: silu, then
-    normalize; state in [d_k, d_v] orientation) and chapter 4 (per-channel alpha
-    multiplies the state rows).
+    normalize; state in [d_k, d_v] orientation; beta = sigmoid(w_beta(x))) and
+    chapter 4 (per-channel alpha multiplies the state rows; alpha = gate(x) is
+    computed from the input, per layer, head and channel).
+  * Page "Kimi K3 注意力三件套", KDA section: alpha comes from a low-rank
+    down-up projection of the input; beta is a single scalar.
 
 Readings adopted where the pages are silent (each also listed in the design doc):
   state K-major [d_k, d_v] with o = S^T q; decay before the delta read; read-out
   after the update; g = log(alpha) as the input; beta one scalar per token and
   head; prologue = conv (width W, zero history at each sequence start, last tap
-  on the current token, no bias) -> SiLU -> x / max(||x||_2, 1e-12) per head.
+  on the current token, no bias) -> SiLU -> x / max(||x||_2, 1e-12) per head;
+  gate: log(alpha) = -softplus(up(down(x)) + b) with a per-channel bias b and no
+  bias inside the projections, beta = sigmoid(w_beta . x) without bias.
 """
 from __future__ import annotations
 
@@ -220,3 +228,54 @@ def prep(x: np.ndarray, w: np.ndarray, cu_seqlens, H: int, d: int, seqs=None) ->
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     seqs = range(len(cu) - 1) if seqs is None else seqs
     return {n: prep_sequence(x[cu[n]:cu[n + 1]], w, H, d) for n in seqs}
+
+
+# --------------------------------------------------------------------------- low-rank gate
+def softplus(x: np.ndarray) -> np.ndarray:
+    """log(1 + e^x) in fp64, written as max(x, 0) + log1p(e^{-|x|}) so no term overflows."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """1 / (1 + e^{-x}) in fp64, evaluated without overflow for either sign of x."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def gate_z(x: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """Down projection of the low-rank gate, fp64: z = x W_down^T.
+
+    x [Ntok, Dm] (stored values), w_down [r, Dm].  The page "Kimi K3 注意力三件套" (KDA
+    section) says alpha is generated by a low-rank down-up projection of the input; this is
+    the "down" half, shared by all heads.  Returns [Ntok, r].
+    """
+    return np.asarray(x, np.float64) @ np.asarray(w_down, np.float64).T
+
+
+def gate_g(z: np.ndarray, w_up: np.ndarray, b: np.ndarray, H: int, d: int) -> np.ndarray:
+    """Up projection and map onto log(alpha), fp64: g = -softplus(z W_up^T + b).
+
+    z [Ntok, r], w_up [H*d, r] (one row per (head, key channel)), b [H*d].  Blog post-114,
+    chapter 4: the gate gives every head and channel its own value computed from the input;
+    the page "Kimi K3 注意力三件套" calls it the "up" half of the low-rank projection.  The
+    pages name no nonlinearity; -softplus maps the pre-activation onto log(alpha) < 0, i.e.
+    alpha = sigmoid(-pre) in (0, 1).  Returns [Ntok, H, d].
+    """
+    pre = np.asarray(z, np.float64) @ np.asarray(w_up, np.float64).T + np.asarray(b, np.float64)[None, :]
+    return (-softplus(pre)).reshape(pre.shape[0], H, d)
+
+
+def gate_beta(x: np.ndarray, w_beta: np.ndarray) -> np.ndarray:
+    """beta = sigmoid(x w_beta^T), fp64: one scalar per token and head (blog post-114, chapter 3
+    code: sigmoid of a linear map of x; page "Kimi K3 注意力三件套": beta is a single scalar).
+    x [Ntok, Dm], w_beta [H, Dm]; returns [Ntok, H]."""
+    return sigmoid(np.asarray(x, np.float64) @ np.asarray(w_beta, np.float64).T)
+
+
+def gate(x, w_down, w_beta, w_up, b, H: int, d: int):
+    """The whole gate in fp64: (z [Ntok, r], beta [Ntok, H], g [Ntok, H, d]), g taken from the
+    unrounded z."""
+    z = gate_z(x, w_down)
+    return z, gate_beta(x, w_beta), gate_g(z, w_up, b, H, d)
