@@ -6,8 +6,10 @@ library is missing, importing works but the first call raises.
 
     o, S = fwd(q, k, v, g, beta, scale=1.0, initial_state=None, cu_seqlens=None)
     o, S = fwd_scalar_gate(q, k, v, g_or_None, beta, ...)    # g [B, T, H]: one decay per head
+    o, S = fwd_lowrank_gate(q, k, v, z, w_up, b_gate, beta, ...)  # log(alpha) formed from z
     o    = decode_step(q, k, v, g, beta, state, scale=1.0)     # state updated in place
     y    = prep(x, conv_w, cu_seqlens=None)
+    z, beta, g = gate(x, w_down, w_beta, w_up=None, b_gate=None, H=..., want_g=False)
 
 Layouts: q, k, g [B, T, H, dk]; v, o [B, T, H, dv]; beta [B, T, H]; states [N, H, dk, dv]
 fp32 with element (i, j) mapping key channel i to value channel j (o = S^T q).  q, k, v
@@ -59,6 +61,10 @@ def lib():
         L.kda_decode_step.restype = I
         L.kda_prep.argtypes = [I, I, I, I, I, P, I, P, P, I, P, P]
         L.kda_prep.restype = I
+        L.kda_gate.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, P, P]
+        L.kda_gate.restype = I
+        L.kda_fwd_lowrank_gate.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, I, P, P, P, F, P, P, P, P, S, P]
+        L.kda_fwd_lowrank_gate.restype = I
         _lib = L
     return _lib
 
@@ -119,7 +125,7 @@ def fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=Non
         output_final_state: bool = True, o=None, final_state=None, workspace=None,
         stream=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunked prefill (kda_fwd).  Returns (o, final_state or None)."""
-    return _fwd(False, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
+    return _fwd("channel", q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
                 final_state, workspace, stream)
 
 
@@ -128,12 +134,52 @@ def fwd_scalar_gate(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu
                     stream=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
     """Chunked prefill with one log-decay per token and head, g [B, T, H], or g = None for
     alpha = 1 (kda_fwd_scalar_gate).  Returns (o, final_state or None)."""
-    return _fwd(True, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
+    return _fwd("scalar", q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
                 final_state, workspace, stream)
 
 
-def _fwd(scalar_gate, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
-         final_state, workspace, stream):
+def fwd_lowrank_gate(q, k, v, z, w_up, b_gate, beta, scale: float = 1.0, initial_state=None, cu_seqlens=None,
+                     output_final_state: bool = True, o=None, final_state=None, workspace=None,
+                     stream=None) -> Tuple["torch.Tensor", Optional["torch.Tensor"]]:
+    """Chunked prefill with the gate in low-rank form (kda_fwd_lowrank_gate): z [B, T, r] bf16,
+    w_up [H*dk, r] bf16, b_gate [H*dk] fp32; log(alpha) = -softplus(z w_up^T + b_gate) is formed in
+    the kernel.  Returns (o, final_state or None)."""
+    return _fwd("lowrank", q, k, v, None, beta, scale, initial_state, cu_seqlens, output_final_state, o,
+                final_state, workspace, stream, lowrank=(z, w_up, b_gate))
+
+
+def gate(x, w_down, w_beta, w_up=None, b_gate=None, H: Optional[int] = None, want_g: bool = False,
+         z=None, beta=None, g=None, stream=None):
+    """Gate prologue (kda_gate) for x [Ntok, Dm] bf16: returns (z [Ntok, r] bf16, beta [Ntok, H] fp32,
+    g [Ntok, H, dk] fp32 or None).  w_down [r, Dm], w_beta [H, Dm], w_up [H*dk, r] (bf16), b_gate
+    [H*dk] fp32; w_up and b_gate are needed only for g."""
+    torch = _torch()
+    Ntok, Dm = x.shape
+    r = w_down.shape[0]
+    H = w_beta.shape[0] if H is None else H
+    _need(x, "x", torch.bfloat16)
+    _need(w_down, "w_down", torch.bfloat16, (r, Dm))
+    _need(w_beta, "w_beta", torch.bfloat16, (H, Dm))
+    dk = 128
+    if w_up is not None:
+        dk = w_up.shape[0] // H
+        _need(w_up, "w_up", torch.bfloat16, (H * dk, r))
+    if want_g:
+        _need(w_up, "w_up", torch.bfloat16)
+        _need(b_gate, "b_gate", torch.float32, (H * dk,))
+    z = torch.empty((Ntok, r), dtype=torch.bfloat16, device=x.device) if z is None else _need(z, "z", torch.bfloat16, (Ntok, r))
+    beta = torch.empty((Ntok, H), dtype=torch.float32, device=x.device) if beta is None else _need(beta, "beta", torch.float32, (Ntok, H))
+    if want_g and g is None:
+        g = torch.empty((Ntok, H, dk), dtype=torch.float32, device=x.device)
+    elif g is not None:
+        _need(g, "g", torch.float32, (Ntok, H, dk))
+    _check(lib().kda_gate(KDA_BF16, Ntok, Dm, H, dk, r, _ptr(x), _ptr(w_down), _ptr(w_beta), _ptr(w_up),
+                          _ptr(b_gate), _ptr(z), _ptr(beta), _ptr(g), _stream(stream)))
+    return z, beta, g
+
+
+def _fwd(kind, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_state, o,
+         final_state, workspace, stream, lowrank=None):
     torch = _torch()
     io = _io_dtype(q)
     B, T, H, dk = q.shape
@@ -142,9 +188,15 @@ def _fwd(scalar_gate, q, k, v, g, beta, scale, initial_state, cu_seqlens, output
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (B, T, H, dk))
     _need(v, "v", q.dtype, (B, T, H, dv))
-    if scalar_gate:
+    if kind == "scalar":
         if g is not None:
             _need(g, "g", torch.float32, (B, T, H))
+    elif kind == "lowrank":
+        z, w_up, b_gate = lowrank
+        r = z.shape[-1]
+        _need(z, "z", torch.bfloat16, (B, T, r))
+        _need(w_up, "w_up", torch.bfloat16, (H * dk, r))
+        _need(b_gate, "b_gate", torch.float32, (H * dk,))
     else:
         _need(g, "g", torch.float32, (B, T, H, dk))
     _need(beta, "beta", torch.float32, (B, T, H))
@@ -163,7 +215,13 @@ def _fwd(scalar_gate, q, k, v, g, beta, scale, initial_state, cu_seqlens, output
     need = fwd_workspace_bytes(io, B, T, H, dk, dv, N, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    fn = lib().kda_fwd_scalar_gate if scalar_gate else lib().kda_fwd
+    if kind == "lowrank":
+        _check(lib().kda_fwd_lowrank_gate(io, B, T, H, dk, dv, _ptr(cu_seqlens), N,
+                                          _ptr(q), _ptr(k), _ptr(v), _ptr(z), r, _ptr(w_up), _ptr(b_gate),
+                                          _ptr(beta), float(scale), _ptr(initial_state), _ptr(final_state),
+                                          _ptr(o), _ptr(workspace), workspace.numel(), _stream(stream)))
+        return o, final_state
+    fn = lib().kda_fwd_scalar_gate if kind == "scalar" else lib().kda_fwd
     _check(fn(io, B, T, H, dk, dv, _ptr(cu_seqlens), N,
               _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
               _ptr(initial_state), _ptr(final_state), _ptr(o),

@@ -79,6 +79,7 @@ kda::FwdArgs fwd_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, con
     a.cu_seqlens = cu_seqlens;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.scalar_gate = false; a.scale = scale;
     a.s0 = s0; a.sN = sN; a.o = o; a.ws = workspace;
+    a.gate_z = nullptr; a.gate_w_up = nullptr; a.gate_b = nullptr; a.gate_r = 0;
     return a;
 }
 
@@ -109,6 +110,54 @@ kda_status_t kda_fwd_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, i
                               final_state, o, workspace);
     a.scalar_gate = true;
     return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                  const int32_t *cu_seqlens, int N, const void *q, const void *k, const void *v,
+                                  const void *z, int r, const void *w_up, const float *b_gate, const float *beta,
+                                  float scale, const float *initial_state, float *final_state, void *o,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    kda_status_t st = check_fwd(kBoth, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, nullptr, beta, initial_state,
+                                final_state, o, workspace, workspace_bytes, true);
+    if (st != KDA_OK) return st;
+    if (r <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (io != KDA_BF16 || r % 32 != 0 || r > 128) return KDA_ERR_UNSUPPORTED;
+    if ((long)N * H == 0) return KDA_OK;
+    if ((long)B * T > 0) {
+        if (!z || !w_up || !b_gate) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(z) || !aligned16(w_up) || !aligned16(b_gate)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, nullptr, beta, scale, initial_state,
+                              final_state, o, workspace);
+    a.gate_z = static_cast<const uint16_t *>(z);
+    a.gate_w_up = static_cast<const uint16_t *>(w_up);
+    a.gate_b = b_gate;
+    a.gate_r = r;
+    return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_gate(kda_dtype_t io, int Ntok, int Dm, int H, int d_k, int r, const void *x, const void *w_down,
+                      const void *w_beta, const void *w_up, const float *b_gate, void *z, float *beta, float *g,
+                      hipStream_t stream) {
+    if (!valid_dtype(io) || Ntok < 0 || Dm <= 0 || H <= 0 || d_k <= 0 || r <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (io != KDA_BF16 || r % 32 != 0 || r > 128 || Dm % 32 != 0 || !supported_d(d_k)) return KDA_ERR_UNSUPPORTED;
+    if (Ntok == 0) return KDA_OK;
+    if (!x || !w_down || !w_beta || !z || !beta) return KDA_ERR_INVALID_ARGUMENT;
+    if (g && (!w_up || !b_gate)) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(x) || !aligned16(w_down) || !aligned16(w_beta) || !aligned16(z) || !aligned16(beta))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (g && (!aligned16(g) || !aligned16(w_up) || !aligned16(b_gate))) return KDA_ERR_INVALID_ARGUMENT;
+    kda::GateArgs a;
+    a.Ntok = Ntok; a.Dm = Dm; a.H = H; a.d = d_k; a.r = r;
+    a.x = static_cast<const uint16_t *>(x);
+    a.w_down = static_cast<const uint16_t *>(w_down);
+    a.w_beta = static_cast<const uint16_t *>(w_beta);
+    a.w_up = static_cast<const uint16_t *>(w_up);
+    a.b = b_gate;
+    a.z = static_cast<uint16_t *>(z);
+    a.beta = beta;
+    a.g = g;
+    return kda::launch_gate(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_fwd_chunk_local(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,

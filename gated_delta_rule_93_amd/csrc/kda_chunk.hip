@@ -349,13 +349,25 @@ __device__ __forceinline__ void local_slot(long id, const int32_t *cu, int N, in
     }
 }
 
-template <bool BF16, int D>
+// The low-rank gate as the chunk-local kernel receives it (see LR below).
+struct LowRankGate {
+    const uint16_t *z;     // [tokens, r] bf16 bits
+    const uint16_t *w_up;  // [H * d, r] bf16 bits
+    const float *b;        // [H * d]
+    int r;                 // multiple of 32, at most 128
+};
+
+// LR: the log-decay is not read from memory but formed here from the low-rank gate,
+// g = -softplus(z W_up^T + b) (one bf16 MFMA per 16x16 tile and 32 rank indices), so the fp32
+// g never travels through HBM.  The values are bitwise those the gate prologue writes out.
+template <bool BF16, int D, bool LR = false>
 __global__ void __launch_bounds__(256, 2)
 chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ k,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta,
-                   const int32_t *__restrict__ cu, int N, int T, int H, long nslots, char *__restrict__ ws) {
+                   const int32_t *__restrict__ cu, int N, int T, int H, long nslots, char *__restrict__ ws,
+                   LowRankGate lr) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     using P = Prec<BF16>;
     using L = WsLayout<BF16, D>;
@@ -383,16 +395,65 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     const int rg = tid / SM::CQ, c4 = (tid % SM::CQ) * 4;
     f32x4 gv[RPG];
     Raw4<TIO> kv[RPG], qv[RPG], vv[RPG];
+    if constexpr (LR) {
+        // g of this chunk and head: wave w forms the 16x16 tiles (tt, ct) for ct = w, w + 4, ...
+        // with A = z rows (tokens), B = W_up rows h*D + channel, k = rank index; rows past a
+        // partial chunk's end are zero.  The tiles go to the G array of LDS, which the
+        // cumulative sum below then reads in its own layout.
+        static_assert(BF16, "the low-rank gate takes bf16 operands");
+        constexpr int NCTW = (D / 16 + 3) / 4;  // column tiles per wave
+        f32x4 acc[4][NCTW];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int u = 0; u < NCTW; ++u) acc[tt][u] = zero4();
+        for (int kb = 0; kb < lr.r / 32; ++kb) {
+            FragB za[4], wb[NCTW];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                const int t = 16 * tt + r16;
+                const uint16_t *zr = lr.z + (pos.tok0 + (t < Cc ? t : 0)) * (long)lr.r + 32 * kb + 4 * grp;
+                za[tt] = frag_bits(*reinterpret_cast<const uint2 *>(zr), *reinterpret_cast<const uint2 *>(zr + 16));
+            }
+#pragma unroll
+            for (int u = 0; u < NCTW; ++u) {
+                const int c = 16 * (wave + 4 * u) + r16;
+                const uint16_t *wr = lr.w_up + ((long)h * D + c) * lr.r + 32 * kb + 4 * grp;
+                wb[u] = frag_bits(*reinterpret_cast<const uint2 *>(wr), *reinterpret_cast<const uint2 *>(wr + 16));
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int u = 0; u < NCTW; ++u) acc[tt][u] = mfma(za[tt], wb[u], acc[tt][u]);
+        }
+#pragma unroll
+        for (int u = 0; u < NCTW; ++u) {
+            const int c = 16 * (wave + 4 * u) + r16;
+            const float bc = lr.b[(long)h * D + c];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int t = 16 * tt + 4 * grp + e;
+                    sm.g.G[t][c] = t < Cc ? gate_log_alpha(acc[tt][u][e] + bc) : 0.f;
+                }
+        }
+    }
     // Rows past the end of a partial chunk read row 0 instead (always valid) and are zeroed
     // afterwards, so every load is unconditional and all of them are in flight together.
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
         const int t = rg * RPG + r;
         const long off = base_in + (t < Cc ? t : 0) * rowstride + c4;
-        gv[r] = *reinterpret_cast<const f32x4 *>(g + off);
+        if constexpr (!LR) gv[r] = *reinterpret_cast<const f32x4 *>(g + off);
         kv[r] = Raw4<TIO>::load(k + off);
         qv[r] = Raw4<TIO>::load(q + off);
         vv[r] = Raw4<TIO>::load(v + off);
+    }
+    if constexpr (LR) {
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) gv[r] = *reinterpret_cast<const f32x4 *>(&sm.g.G[rg * RPG + r][c4]);
     }
     const float bt_raw = beta[(pos.tok0 + (tid < Cc ? tid : 0)) * H + h];
 #pragma unroll
@@ -1132,14 +1193,15 @@ long fwd_chunk_slots(int B, int T, int N, bool varlen) {
     return varlen ? (long)N + ncs : (long)B * ncs;
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, bool LR = false>
 static hipError_t launch_local_t(const FwdArgs &a, hipStream_t st) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     const long slots = fwd_chunk_slots(a.B, a.T, a.N, a.cu_seqlens != nullptr);
     if (slots <= 0 || a.H <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_local_kernel<BF16, D>), dim3((unsigned)(slots * a.H)), dim3(256), 0, st,
+    const LowRankGate lr{a.gate_z, a.gate_w_up, a.gate_b, a.gate_r};
+    hipLaunchKernelGGL((chunk_local_kernel<BF16, D, LR>), dim3((unsigned)(slots * a.H)), dim3(256), 0, st,
                        (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T,
-                       a.H, slots, static_cast<char *>(a.ws));
+                       a.H, slots, static_cast<char *>(a.ws), lr);
     return hipGetLastError();
 }
 
@@ -1198,6 +1260,9 @@ hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {
     if (a.scalar_gate) {
         if (a.bf16) return a.dk == 128 ? launch_local_scalar_t<true, 128>(a, st) : launch_local_scalar_t<true, 64>(a, st);
         return a.dk == 128 ? launch_local_scalar_t<false, 128>(a, st) : launch_local_scalar_t<false, 64>(a, st);
+    }
+    if (a.gate_z) {  // low-rank gate: bf16 only (checked by the caller)
+        return a.dk == 128 ? launch_local_t<true, 128, true>(a, st) : launch_local_t<true, 64, true>(a, st);
     }
     if (a.bf16) return a.dk == 128 ? launch_local_t<true, 128>(a, st) : launch_local_t<true, 64>(a, st);
     return a.dk == 128 ? launch_local_t<false, 128>(a, st) : launch_local_t<false, 64>(a, st);

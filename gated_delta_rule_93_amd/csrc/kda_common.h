@@ -58,6 +58,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// log(alpha) of the low-rank gate from its pre-activation x: -softplus(x) = -log(1 + e^x),
+// evaluated as -(max(x, 0) + log(1 + e^{-|x|})) with the hardware base-2 exp and log, so no
+// intermediate overflows.  The gate prologue and the fused chunk-local kernel both call this
+// one function, so the log-decay they produce is bitwise the same.
+__device__ __forceinline__ float gate_log_alpha(float x) {
+    const float e = fast_exp2(-fabsf(x) * kLog2e);  // in (0, 1]
+    return -(fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * kLn2);
+}
+
 // ---------------------------------------------------------------- MFMA operand fragments
 //
 // One fragment holds, for one lane, the 8 "k-slot" values of a 16 x 32 (rows x k) operand
@@ -105,6 +116,12 @@ __device__ __forceinline__ FragF make_fragF(const float *x) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) f.v[s] = x[s];
     return f;
+}
+
+// Fragment from stored bf16 bits: slots 0..3 from `lo` (4 consecutive elements of the k block,
+// starting at 4 grp), slots 4..7 from `hi` (starting at 16 + 4 grp), as the k-slot map requires.
+__device__ __forceinline__ FragB frag_bits(uint2 lo, uint2 hi) {
+    return FragB{__builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y))};
 }
 
 __device__ __forceinline__ f32x4 mfma(const FragB &a, const FragB &b, f32x4 c) {

@@ -35,6 +35,11 @@ struct FwdArgs {
     const void *q, *k, *v;
     const float *g, *beta;
     bool scalar_gate;           // g is [B, T, H] (one log-decay per token and head), or NULL (alpha = 1)
+    // Low-rank gate (g == NULL, bf16 only): log(alpha) = -softplus(z W_up^T + b), formed in the
+    // chunk-local kernel; z [tokens, r], w_up [H*dk, r] (bf16 bits), b [H*dk]; r % 32 == 0, r <= 128.
+    const uint16_t *gate_z, *gate_w_up;
+    const float *gate_b;
+    int gate_r;
     float scale;
     const float *s0;
     float *sN;
@@ -47,5 +52,15 @@ long fwd_chunk_slots(int B, int T, int N, bool varlen);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);          // both phases
 hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st);    // chunk-local phase
 hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st);     // state-scan phase
+
+struct GateArgs {
+    int Ntok, Dm, H, d, r;
+    const uint16_t *x, *w_down, *w_beta, *w_up;  // bf16 bits: [Ntok, Dm], [r, Dm], [H, Dm], [H*d, r]
+    const float *b;                              // [H*d]
+    uint16_t *z;                                 // [Ntok, r] bf16
+    float *beta;                                 // [Ntok, H]
+    float *g;                                    // [Ntok, H, d] or NULL
+};
+hipError_t launch_gate(const GateArgs &a, hipStream_t st);
 
 }  // namespace kda

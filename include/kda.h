@@ -137,6 +137,54 @@ kda_status_t kda_fwd_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, i
                                  hipStream_t stream);
 
 /*
+ * Low-rank gate.  The page "Kimi K3 注意力三件套" (KDA section) says the per-channel alpha comes
+ * from a low-rank down-up projection of the layer input x, and beta is one scalar; blog post-114
+ * has beta = sigmoid(w_beta(x)) (chapter 3) and a gate per head and channel computed from x
+ * (chapter 4).  The pages give no nonlinearity for alpha; the one used here is
+ *     z      = x W_down^T                         rank r, shared by all heads
+ *     log a  = g = -softplus(z W_up^T + b)        per (token, head, key channel), so 0 < alpha < 1
+ *     beta   = sigmoid(x w_beta^T)                per (token, head)
+ * Weights use the [out, in] layout.  bf16 operands, fp32 arithmetic; z is stored in bf16.
+ */
+
+/*
+ * kda_gate -- the gate prologue for Ntok tokens: writes z and beta, and g when g != NULL.
+ * The g it writes is bitwise the one kda_fwd_lowrank_gate forms internally from the same z.
+ *
+ *   io      KDA_BF16 (x, weights and z); anything else returns KDA_ERR_UNSUPPORTED
+ *   x       [Ntok, Dm] bf16 (Dm a multiple of 32)
+ *   w_down  [r, Dm] bf16 (r a multiple of 32, at most 128);  w_beta [H, Dm] bf16
+ *   w_up    [H * d_k, r] bf16 and b_gate [H * d_k] fp32: required only when g != NULL
+ *   z       [Ntok, r] bf16 out;  beta [Ntok, H] fp32 out;  g [Ntok, H, d_k] fp32 out or NULL
+ *   Supported: d_k in {64, 128}.  All buffers device, 16-byte aligned, caller-owned.
+ */
+kda_status_t kda_gate(kda_dtype_t io, int Ntok, int Dm, int H, int d_k, int r,
+                      const void *x, const void *w_down, const void *w_beta,
+                      const void *w_up, const float *b_gate,
+                      void *z, float *beta, float *g, hipStream_t stream);
+
+/*
+ * kda_fwd_lowrank_gate -- kda_fwd with the gate given by its low-rank form instead of g:
+ * log(alpha) = -softplus(z W_up^T + b) is formed inside the chunk-local kernel, so the fp32 g
+ * (d_k floats per token and head) is never written to or read from HBM.  Bitwise equal to
+ * kda_gate(..., g) followed by kda_fwd(..., g, ...).
+ *
+ *   io      KDA_BF16 only (q, k, v, o, z, w_up); KDA_F32 returns KDA_ERR_UNSUPPORTED
+ *   z       [B, T, r] bf16 (tokens laid out as q's);  r a multiple of 32, at most 128
+ *   w_up    [H * d_k, r] bf16;  b_gate [H * d_k] fp32
+ *   all other arguments, layouts, the workspace (kda_fwd_workspace_bytes) and the error
+ *   behaviour are those of kda_fwd.
+ */
+kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                  const int32_t *cu_seqlens, int N,
+                                  const void *q, const void *k, const void *v,
+                                  const void *z, int r, const void *w_up, const float *b_gate,
+                                  const float *beta, float scale,
+                                  const float *initial_state, float *final_state,
+                                  void *o, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
+/*
  * kda_decode_step -- one token of the recurrence for N independent sequences, in place.
  * The state stays resident in HBM; each call reads and rewrites it once
  * (the fixed-size state of the course page's section 2 makes each step O(1) in the

@@ -135,3 +135,61 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         kda.lib()
+
+
+def lowrank_call(**over):
+    a = dict(io=kda.KDA_BF16, B=1, T=64, H=1, dk=128, dv=128, cu=None, N=1, q=FAKE, k=FAKE, v=FAKE, z=FAKE, r=32,
+             w_up=FAKE, b=FAKE, beta=FAKE, scale=1.0, s0=None, sN=None, o=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(over)
+    return kda.lib().kda_fwd_lowrank_gate(a["io"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["cu"], a["N"],
+                                          a["q"], a["k"], a["v"], a["z"], a["r"], a["w_up"], a["b"], a["beta"],
+                                          a["scale"], a["s0"], a["sN"], a["o"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(io=5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(N=2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(z=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(w_up=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(b=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(z=FAKE + 8), kda.KDA_ERR_INVALID_ARGUMENT),              # misaligned z
+    (dict(r=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(r=48), kda.KDA_ERR_UNSUPPORTED),                         # not a multiple of 32
+    (dict(r=160), kda.KDA_ERR_UNSUPPORTED),                        # above 128
+    (dict(io=kda.KDA_F32), kda.KDA_ERR_UNSUPPORTED),               # bf16 only
+    (dict(dk=96, dv=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(ws=None), kda.KDA_ERR_WORKSPACE),
+])
+def test_fwd_lowrank_gate_rejects(over, code):
+    assert lowrank_call(**over) == code
+
+
+def gate_call(**over):
+    a = dict(io=kda.KDA_BF16, Ntok=100, Dm=256, H=4, dk=128, r=32, x=FAKE, w_down=FAKE, w_beta=FAKE, w_up=FAKE,
+             b=FAKE, z=FAKE, beta=FAKE, g=FAKE, stream=None)
+    a.update(over)
+    return kda.lib().kda_gate(a["io"], a["Ntok"], a["Dm"], a["H"], a["dk"], a["r"], a["x"], a["w_down"],
+                              a["w_beta"], a["w_up"], a["b"], a["z"], a["beta"], a["g"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(io=5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(Ntok=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(H=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(x=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(beta=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(w_up=None), kda.KDA_ERR_INVALID_ARGUMENT),               # g requested without w_up
+    (dict(x=FAKE + 2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(Dm=100), kda.KDA_ERR_UNSUPPORTED),                       # width not a multiple of 32
+    (dict(r=16), kda.KDA_ERR_UNSUPPORTED),
+    (dict(io=kda.KDA_F32), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=96), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_gate_rejects(over, code):
+    assert gate_call(**over) == code
+
+
+def test_gate_empty_and_g_optional():
+    assert gate_call(Ntok=0) == kda.KDA_OK
+    assert gate_call(Ntok=0, g=None, w_up=None, b=None) == kda.KDA_OK
+    assert lowrank_call(H=0, ws=None, wsb=0) == kda.KDA_OK
