@@ -13,7 +13,7 @@ The same run also measures
   * the fp64 CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel times come from HIP events recorded on the stream the kernels run on.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,scalar,long,varlen,cpu,copy]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,scalar,gate,long,varlen,cpu,copy]
 Prints one JSON line.  `--only copy` runs a plain 256 MiB device copy (a kernel of known size
 used to calibrate the FETCH_SIZE / WRITE_SIZE counters of profiler runs).
 The roofline "traffic" figure comes from profiles/traffic.json (counter runs of this same
@@ -267,6 +267,66 @@ def bench_scalar_gate(torch, kda, dev, reps=20):
     return out
 
 
+def bench_lowrank_gate(torch, kda, dev, reps=20):
+    """The prefill batch (B=4, H=16, T=4096, d=128, bf16) with the gate in low-rank form: hidden
+    width 2048, rank 32.  Times the gate prologue (z and beta; and with log alpha written out), the
+    operator fed with that log alpha (kda_fwd) and the fused operator (kda_fwd_lowrank_gate), and
+    the two layer totals: prologue(g) + kda_fwd versus prologue(z) + fused."""
+    B, T, H, d, r, Dm = 4, 4096, 16, 128, 32, 2048
+    n = B * T
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93240)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    x = rnd(n, Dm).to(torch.bfloat16)
+    w_down = (rnd(r, Dm) / Dm ** 0.5).to(torch.bfloat16)
+    w_beta = (rnd(H, Dm) / Dm ** 0.5).to(torch.bfloat16)
+    w_up = (rnd(H * d, r) / r ** 0.5).to(torch.bfloat16)
+    b = (2.0 + 0.5 * rnd(H * d)).contiguous()
+    q, k = _unit_bf16(rnd(B, T, H, d)), _unit_bf16(rnd(B, T, H, d))
+    v = rnd(B, T, H, d).to(torch.bfloat16)
+    z = torch.empty((n, r), dtype=torch.bfloat16, device=dev)
+    beta = torch.empty((n, H), dtype=torch.float32, device=dev)
+    g = torch.empty((n, H, d), dtype=torch.float32, device=dev)
+    o = torch.empty((B, T, H, d), dtype=torch.bfloat16, device=dev)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    nws = kda.fwd_workspace_bytes(kda.KDA_BF16, B, T, H, d, d, B, False)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    L = kda.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: None if t is None else t.data_ptr()
+
+    def prologue(gp):
+        assert L.kda_gate(kda.KDA_BF16, n, Dm, H, d, r, p(x), p(w_down), p(w_beta), p(w_up), p(b), p(z), p(beta),
+                          gp, st) == 0
+
+    def fwd_g():
+        assert L.kda_fwd(kda.KDA_BF16, B, T, H, d, d, None, B, p(q), p(k), p(v), p(g), p(beta), 1.0, None, p(S),
+                         p(o), p(ws), nws, st) == 0
+
+    def fwd_fused():
+        assert L.kda_fwd_lowrank_gate(kda.KDA_BF16, B, T, H, d, d, None, B, p(q), p(k), p(v), p(z), r, p(w_up), p(b),
+                                      p(beta), 1.0, None, p(S), p(o), p(ws), nws, st) == 0
+
+    prologue(p(g))
+    fns = {"prologue_z_beta": lambda: prologue(None), "prologue_with_log_alpha": lambda: prologue(p(g)),
+           "fwd_with_log_alpha": fwd_g, "fwd_fused": fwd_fused,
+           "layer_unfused": lambda: (prologue(p(g)), fwd_g()), "layer_fused": lambda: (prologue(None), fwd_fused())}
+    out = {"workload": "KDA prefill B=4 H=16 T=4096 d=128 bf16 with the gate from hidden states of width 2048 "
+                       "through rank 32 (log alpha = -softplus(z W_up^T + b), beta = sigmoid(x w_beta^T))"}
+    for label, fn in fns.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        out[label + "_ms"] = time_events(fn, reps, torch)
+    x_bytes, zb_bytes, g_bytes = n * Dm * 2, n * (r * 2 + H * 4), n * H * d * 4
+    out["prologue_z_beta_GBs"] = (x_bytes + zb_bytes) / out["prologue_z_beta_ms"] / 1e6
+    out["prologue_z_beta_hbm_frac"] = out["prologue_z_beta_GBs"] / HBM_PEAK_GBS
+    out["prologue_with_log_alpha_GBs"] = (x_bytes + zb_bytes + g_bytes) / out["prologue_with_log_alpha_ms"] / 1e6
+    out["layer_fused_tokens_per_s"] = n / (out["layer_fused_ms"] / 1e3)
+    out["layer_unfused_tokens_per_s"] = n / (out["layer_unfused_ms"] / 1e3)
+    return out
+
+
 def bench_varlen_layer(torch, kda, dev, reps=5):
     """Varlen layer: 64 packed sequences (lengths U[512, 16384] from the workload seed), H=32, d=128:
     prologue on raw q and k (width 4), then the chunked prefill with per-sequence S_0 ~ N(0, 0.02)."""
@@ -374,8 +434,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,prep,scalar,long,varlen,cpu",
-                    help="comma list of prefill, decode, prep, scalar, long, varlen, cpu, copy")
+    ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,long,varlen,cpu",
+                    help="comma list of prefill, decode, prep, scalar, gate, long, varlen, cpu, copy")
     args = ap.parse_args()
     only = set(x.strip() for x in args.only.split(",") if x.strip())
     if args.gpus != 1:
@@ -395,6 +455,8 @@ def main():
             out["prep"] = bench_prep(args, torch, kda, dev)
         if "scalar" in only:
             out["scalar_gate"] = bench_scalar_gate(torch, kda, dev)
+        if "gate" in only:
+            out["lowrank_gate"] = bench_lowrank_gate(torch, kda, dev)
         if "long" in only:
             out["long_context"] = bench_long(torch, kda, dev)
         if "varlen" in only:
@@ -458,6 +520,9 @@ def main():
     if "scalar" in only:
         log("scalar gate ...")
         out["scalar_gate"] = bench_scalar_gate(torch, kda, dev)
+    if "gate" in only:
+        log("low-rank gate ...")
+        out["lowrank_gate"] = bench_lowrank_gate(torch, kda, dev)
     if "long" in only:
         log("long context ...")
         out["long_context"] = bench_long(torch, kda, dev)

@@ -395,10 +395,21 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     const int rg = tid / SM::CQ, c4 = (tid % SM::CQ) * 4;
     f32x4 gv[RPG];
     Raw4<TIO> kv[RPG], qv[RPG], vv[RPG];
+    // Rows past the end of a partial chunk read row 0 instead (always valid) and are zeroed
+    // afterwards, so every load is unconditional and all of them are in flight together.
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        const int t = rg * RPG + r;
+        const long off = base_in + (t < Cc ? t : 0) * rowstride + c4;
+        if constexpr (!LR) gv[r] = *reinterpret_cast<const f32x4 *>(g + off);
+        kv[r] = Raw4<TIO>::load(k + off);
+        qv[r] = Raw4<TIO>::load(q + off);
+        vv[r] = Raw4<TIO>::load(v + off);
+    }
     if constexpr (LR) {
-        // g of this chunk and head: wave w forms the 16x16 tiles (tt, ct) for ct = w, w + 4, ...
-        // with A = z rows (tokens), B = W_up rows h*D + channel, k = rank index; rows past a
-        // partial chunk's end are zero.  The tiles go to the G array of LDS, which the
+        // g of this chunk and head (after the q, k, v loads above are in flight): wave w forms
+        // the 16x16 tiles (tt, ct) for ct = w, w + 4, ... with A = z rows (tokens), B = W_up rows
+        // h*D + channel, k = rank index; rows past a partial chunk's end are zero.  The tiles go to the G array of LDS, which the
         // cumulative sum below then reads in its own layout.
         static_assert(BF16, "the low-rank gate takes bf16 operands");
         constexpr int NCTW = (D / 16 + 3) / 4;  // column tiles per wave
@@ -438,17 +449,6 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                     sm.g.G[t][c] = t < Cc ? gate_log_alpha(acc[tt][u][e] + bc) : 0.f;
                 }
         }
-    }
-    // Rows past the end of a partial chunk read row 0 instead (always valid) and are zeroed
-    // afterwards, so every load is unconditional and all of them are in flight together.
-#pragma unroll
-    for (int r = 0; r < RPG; ++r) {
-        const int t = rg * RPG + r;
-        const long off = base_in + (t < Cc ? t : 0) * rowstride + c4;
-        if constexpr (!LR) gv[r] = *reinterpret_cast<const f32x4 *>(g + off);
-        kv[r] = Raw4<TIO>::load(k + off);
-        qv[r] = Raw4<TIO>::load(q + off);
-        vv[r] = Raw4<TIO>::load(v + off);
     }
     if constexpr (LR) {
         __syncthreads();

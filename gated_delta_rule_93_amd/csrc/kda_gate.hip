@@ -5,10 +5,10 @@
 // projection of the input and beta is one scalar; blog post-114, chapter 3 has beta as the
 // sigmoid of a linear map of x and chapter 4 a gate per head and channel computed from x.
 //
-// One 256-thread workgroup per 64 tokens; wave w owns tokens 16w .. 16w+15 of the block.  The
-// down projection and the beta projection are one skinny bf16 MFMA product over the model width
-// (x rows as A fragments, the stacked weight rows [W_down; w_beta] as B fragments), four column
-// tiles at a time.  z is rounded to bf16 once; the optional log(alpha) is formed from those
+// One 512-thread workgroup per 64 tokens.  The down projection and the beta projection are one
+// skinny bf16 MFMA product over the model width (x rows as A fragments, the stacked weight rows
+// [W_down; w_beta] as B fragments), four column tiles at a time, the width split over two waves
+// per 16-token row tile.  z is rounded to bf16 once; the optional log(alpha) is formed from those
 // rounded values by the same MFMA and the same nonlinearity as the fused chunk-local kernel, so
 // the two paths agree bit for bit.
 #include "kda_common.h"
@@ -20,86 +20,134 @@ namespace {
 
 constexpr int kGateTokens = 64;
 
-// B fragment of row `row` of a [rows, ld] bf16 matrix, k block kb (zero past `rows`).
-__device__ __forceinline__ FragB row_frag(const uint16_t *w, int rows, long ld, int row, int kb, int grp) {
-    if (row >= rows) return frag_bits(make_uint2(0u, 0u), make_uint2(0u, 0u));
-    const uint16_t *p = w + (long)row * ld + 32 * kb + 4 * grp;
-    return frag_bits(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
-}
+// Operands of the projections over the model width: lane (grp, r16) supplies row r16 and the 8
+// consecutive width indices 32 kb + 8 grp .. + 7 (one 16-byte load).  A and B use the same map,
+// so the MFMA sums over all 32 indices of the block; this is not the k-slot map of the other
+// kernels, which only matters for fragments shared with them (z below is not loaded this way).
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + fast_exp2(-x * kLog2e)); }
 
 }  // namespace
 
-__global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
+// Waves (tt, kh): row tile tt = w & 3 (16 tokens), half kh = w >> 2 of the model width for the
+// projections and of the log-alpha columns.  The width loop issues the loads of four k blocks
+// before their MFMAs, so each wave has 20 loads in flight.
+__global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
     __shared__ uint16_t zs[kGateTokens][128 + 8];  // the block's rounded z rows (for log(alpha))
+    __shared__ f32x4 red[4][4][64];                // upper-half partial sums of four column tiles
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    const int tt = wave & 3, kh = wave >> 2;
     const long tok0 = (long)blockIdx.x * kGateTokens;
-    const long arow = tok0 + 16 * wave + r16;                      // this lane's A row (token)
-    const uint16_t *xr = a.x + (arow < a.Ntok ? arow : a.Ntok - 1) * (long)a.Dm + 4 * grp;
+    const long arow = tok0 + 16 * tt + r16;                      // this lane's A row (token)
+    const int xrow = (int)(arow < a.Ntok ? arow : a.Ntok - 1);
     const int nzt = a.r / 16, nbt = (a.H + 15) / 16, nct = nzt + nbt;
-    const int nkb = a.Dm / 32;
+    const int nkb = a.Dm / 32, kb0 = kh * (nkb / 2), kb1 = kh ? nkb : nkb / 2;
 
-    // ---- z and beta: column tiles ct < nzt are rank indices, the rest heads
+    // ---- z and beta: column tiles ct < nzt are rank indices, the rest heads.  The loop over the
+    // width is branch-free (every tile of the group is loaded from a valid row and masked), so
+    // the unrolled iterations keep their loads in flight together.
+    const uint16_t *xp = a.x + (long)xrow * a.Dm + 8 * grp;
     for (int cg = 0; cg < nct; cg += 4) {
+        const uint16_t *wp[4];
+        bool wv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ct = cg + u;
+            const bool zt = ct < nzt;
+            const int row = zt ? 16 * ct + r16 : 16 * (ct - nzt) + r16;
+            wv[u] = zt || (ct < nct && row < a.H);
+            wp[u] = (wv[u] ? (zt ? a.w_down : a.w_beta) + (long)row * a.Dm : a.w_down) + 8 * grp;
+        }
         f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-        for (int kb = 0; kb < nkb; ++kb) {
-            const FragB xa = frag_bits(*reinterpret_cast<const uint2 *>(xr + 32 * kb),
-                                       *reinterpret_cast<const uint2 *>(xr + 32 * kb + 16));
+        // four k blocks per step: all 20 loads are issued before the 16 MFMAs that use them
+        for (int kb = kb0; kb < kb1; kb += 4) {
+            u32x4 xv[4], wv4[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kk = min(kb + i, kb1 - 1);  // past the end: a valid block, zeroed below
+                xv[i] = ld16(xp + 32 * kk);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) wv4[i][u] = ld16(wp[u] + 32 * kk);
+            }
+            // The loaded values pass through an empty asm statement: every load is issued before it
+            // and no MFMA moves above it, so all 20 loads are in flight together (left alone, the
+            // scheduler issues each load just before its MFMA).
+            asm volatile("" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]),
+                              "+v"(wv4[0][0]), "+v"(wv4[0][1]), "+v"(wv4[0][2]), "+v"(wv4[0][3]),
+                              "+v"(wv4[1][0]), "+v"(wv4[1][1]), "+v"(wv4[1][2]), "+v"(wv4[1][3]),
+                              "+v"(wv4[2][0]), "+v"(wv4[2][1]), "+v"(wv4[2][2]), "+v"(wv4[2][3]),
+                              "+v"(wv4[3][0]), "+v"(wv4[3][1]), "+v"(wv4[3][2]), "+v"(wv4[3][3]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (kb + i >= kb1) xv[i] = u32x4{0u, 0u, 0u, 0u};
+                const FragB xa{__builtin_bit_cast(bf16x8, xv[i])};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const u32x4 w = wv[u] ? wv4[i][u] : u32x4{0u, 0u, 0u, 0u};
+                    acc[u] = mfma(xa, FragB{__builtin_bit_cast(bf16x8, w)}, acc[u]);
+                }
+            }
+        }
+        // add the two halves in a fixed order (lower + upper), so the result is deterministic
+        if (kh == 1) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) red[tt][u][lane] = acc[u];
+        }
+        __syncthreads();
+        if (kh == 0) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int ct = cg + u;
                 if (ct >= nct) break;
-                const FragB wb = ct < nzt ? row_frag(a.w_down, a.r, a.Dm, 16 * ct + r16, kb, grp)
-                                          : row_frag(a.w_beta, a.H, a.Dm, 16 * (ct - nzt) + r16, kb, grp);
-                acc[u] = mfma(xa, wb, acc[u]);
-            }
-        }
+                acc[u] += red[tt][u][lane];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int ct = cg + u;
-            if (ct >= nct) break;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int trow = 16 * wave + 4 * grp + e;  // token row within the block
-                const long tok = tok0 + trow;
-                if (ct < nzt) {
-                    const int j = 16 * ct + r16;
-                    const uint16_t zb = __builtin_bit_cast(uint16_t, (__bf16)acc[u][e]);  // round to nearest even
-                    zs[trow][j] = zb;
-                    if (tok < a.Ntok) a.z[tok * a.r + j] = zb;
-                } else {
-                    const int hh = 16 * (ct - nzt) + r16;
-                    if (tok < a.Ntok && hh < a.H) a.beta[tok * a.H + hh] = sigmoidf_(acc[u][e]);
+                for (int e = 0; e < 4; ++e) {
+                    const int trow = 16 * tt + 4 * grp + e;  // token row within the block
+                    const long tok = tok0 + trow;
+                    if (ct < nzt) {
+                        const int j = 16 * ct + r16;
+                        const uint16_t zb = __builtin_bit_cast(uint16_t, (__bf16)acc[u][e]);  // round to nearest even
+                        zs[trow][j] = zb;
+                        if (tok < a.Ntok) a.z[tok * a.r + j] = zb;
+                    } else {
+                        const int hh = 16 * (ct - nzt) + r16;
+                        if (tok < a.Ntok && hh < a.H) a.beta[tok * a.H + hh] = sigmoidf_(acc[u][e]);
+                    }
                 }
             }
         }
+        __syncthreads();  // red is reused by the next column group; zs is complete after the last
     }
     if (!a.g) return;  // uniform over the grid
 
-    // ---- log(alpha) = -softplus(z W_up^T + b) from the rounded z (A fragments read back from LDS)
-    __syncthreads();
+    // ---- log(alpha) = -softplus(z W_up^T + b) from the rounded z (A fragments read back from LDS);
+    // wave (tt, kh) forms row tile tt for half kh of the columns
     const int nrk = a.r / 32;
     FragB za[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         if (kb >= nrk) break;
-        const uint16_t *p = &zs[16 * wave + r16][32 * kb + 4 * grp];
+        const uint16_t *p = &zs[16 * tt + r16][32 * kb + 4 * grp];
         za[kb] = frag_bits(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
     }
-    const int ncols = a.H * a.d;
-    for (int ct = 0; ct < ncols / 16; ++ct) {
+    const int ncols = a.H * a.d, nt = ncols / 16, ct0 = kh * (nt / 2), ct1 = kh ? nt : nt / 2;
+#pragma unroll 4
+    for (int ct = ct0; ct < ct1; ++ct) {
         const int c = 16 * ct + r16;
+        const uint16_t *wr = a.w_up + (long)c * a.r + 4 * grp;
         f32x4 acc = zero4();
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             if (kb >= nrk) break;
-            acc = mfma(za[kb], row_frag(a.w_up, ncols, a.r, c, kb, grp), acc);
+            acc = mfma(za[kb], frag_bits(*reinterpret_cast<const uint2 *>(wr + 32 * kb),
+                                         *reinterpret_cast<const uint2 *>(wr + 32 * kb + 16)), acc);
         }
         const float bc = a.b[c];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const long tok = tok0 + 16 * wave + 4 * grp + e;
+            const long tok = tok0 + 16 * tt + 4 * grp + e;
             if (tok < a.Ntok) a.g[tok * ncols + c] = gate_log_alpha(acc[e] + bc);
         }
     }
@@ -108,7 +156,7 @@ __global__ void __launch_bounds__(256) gate_kernel(GateArgs a) {
 hipError_t launch_gate(const GateArgs &a, hipStream_t st) {
     if (a.Ntok <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)((a.Ntok + kGateTokens - 1) / kGateTokens);
-    hipLaunchKernelGGL(gate_kernel, dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(gate_kernel, dim3(blocks), dim3(512), 0, st, a);
     return hipGetLastError();
 }
 
