@@ -10,6 +10,9 @@ library is missing, importing works but the first call raises.
     o    = decode_step(q, k, v, g, beta, state, scale=1.0)     # state updated in place
     y    = prep(x, conv_w, cu_seqlens=None)
     z, beta, g = gate(x, w_down, w_beta, w_up=None, b_gate=None, H=..., want_g=False)
+    h          = attnres(blocks, w, eps)                     # Block AttnRes read-out
+    o, lse     = attnres_inter(blocks, W, eps)               # phase 1 for L layers
+    h          = attnres_merge(partial, w, o_l, lse_l, eps)  # phase 2 for one layer
 
 Layouts: q, k, g [B, T, H, dk]; v, o [B, T, H, dv]; beta [B, T, H]; states [N, H, dk, dv]
 fp32 with element (i, j) mapping key channel i to value channel j (o = S^T q).  q, k, v
@@ -65,6 +68,14 @@ def lib():
         L.kda_gate.restype = I
         L.kda_fwd_lowrank_gate.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, I, P, P, P, F, P, P, P, P, S, P]
         L.kda_fwd_lowrank_gate.restype = I
+        L.kda_attnres.argtypes = [I, I, I, I, P, P, F, P, P]
+        L.kda_attnres.restype = I
+        L.kda_attnres_inter_workspace_bytes.argtypes = [I, I, I]
+        L.kda_attnres_inter_workspace_bytes.restype = S
+        L.kda_attnres_inter.argtypes = [I, I, I, I, I, P, P, F, P, P, P, S, P]
+        L.kda_attnres_inter.restype = I
+        L.kda_attnres_merge.argtypes = [I, I, I, P, P, F, P, P, P, P]
+        L.kda_attnres_merge.restype = I
         _lib = L
     return _lib
 
@@ -268,3 +279,59 @@ def prep(x, conv_w, cu_seqlens=None, y=None, stream=None):
     _check(lib().kda_prep(io, B, T, H, d, _ptr(cu_seqlens), N, _ptr(x), _ptr(conv_w), W, _ptr(y),
                           _stream(stream)))
     return y
+
+
+def _block_ptrs(blocks):
+    """blocks: a list of [T, d] bf16 device tensors, or one [n, T, d] tensor -> (ctypes array, n, T, d)."""
+    torch = _torch()
+    if isinstance(blocks, torch.Tensor):
+        blocks = list(blocks.unbind(0))
+    if not blocks:
+        raise ValueError("at least one block is required")
+    T, d = blocks[0].shape
+    for i, b in enumerate(blocks):
+        _need(b, f"blocks[{i}]", torch.bfloat16, (T, d))
+    arr = (ctypes.c_void_p * len(blocks))(*[b.data_ptr() for b in blocks])
+    return arr, len(blocks), T, d
+
+
+def attnres(blocks, w, eps: float = 1e-6, h=None, stream=None):
+    """Block AttnRes read-out of one layer (kda_attnres): h [T, d] = sum_n softmax_n(w . norm(V_n)) V_n."""
+    torch = _torch()
+    arr, n, T, d = _block_ptrs(blocks)
+    _need(w, "w", torch.bfloat16, (d,))
+    h = torch.empty((T, d), dtype=torch.bfloat16, device=w.device) if h is None else _need(h, "h", torch.bfloat16, (T, d))
+    _check(lib().kda_attnres(KDA_BF16, n, T, d, arr, _ptr(w), float(eps), _ptr(h), _stream(stream)))
+    return h
+
+
+def attnres_inter(blocks, W, eps: float = 1e-6, o=None, lse=None, workspace=None, stream=None):
+    """Phase 1 of the two-phase AttnRes (kda_attnres_inter) for the L = W.shape[0] layers:
+    returns (o [L, T, d] bf16, lse [L, T] fp32)."""
+    torch = _torch()
+    arr, n, T, d = _block_ptrs(blocks)
+    L = W.shape[0]
+    _need(W, "W", torch.bfloat16, (L, d))
+    o = torch.empty((L, T, d), dtype=torch.bfloat16, device=W.device) if o is None else _need(o, "o", torch.bfloat16, (L, T, d))
+    lse = torch.empty((L, T), dtype=torch.float32, device=W.device) if lse is None else _need(lse, "lse", torch.float32, (L, T))
+    need = int(lib().kda_attnres_inter_workspace_bytes(n, L, T))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=W.device)
+    _check(lib().kda_attnres_inter(KDA_BF16, n, L, T, d, arr, _ptr(W), float(eps), _ptr(o), _ptr(lse),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o, lse
+
+
+def attnres_merge(partial, w, o_l, lse_l, eps: float = 1e-6, h=None, stream=None):
+    """Phase 2 for one layer (kda_attnres_merge): merges the partial block [T, d] into the layer's
+    phase-1 result (o_l [T, d], lse_l [T]); returns h [T, d]."""
+    torch = _torch()
+    T, d = partial.shape
+    _need(partial, "partial", torch.bfloat16, (T, d))
+    _need(w, "w", torch.bfloat16, (d,))
+    _need(o_l, "o_l", torch.bfloat16, (T, d))
+    _need(lse_l, "lse_l", torch.float32, (T,))
+    h = torch.empty_like(partial) if h is None else _need(h, "h", torch.bfloat16, (T, d))
+    _check(lib().kda_attnres_merge(KDA_BF16, T, d, _ptr(partial), _ptr(w), float(eps), _ptr(o_l), _ptr(lse_l),
+                                   _ptr(h), _stream(stream)))
+    return h

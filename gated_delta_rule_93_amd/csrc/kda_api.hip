@@ -6,6 +6,7 @@
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool supported_d(int d) { return d == 64 || d == 128; }
 bool valid_dtype(kda_dtype_t io) { return io == KDA_F32 || io == KDA_BF16; }
 
@@ -30,6 +31,11 @@ size_t kda_fwd_workspace_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int
     if (varlen && B != 1) return 0;
     const long slots = kda::fwd_chunk_slots(B, T, N, varlen != 0);
     return (size_t)slots * (size_t)H * kda::fwd_bytes_per_chunk_head(io == KDA_BF16, d_k);
+}
+
+size_t kda_attnres_inter_workspace_bytes(int n, int L, int T) {
+    if (n < 1 || n > kda::kAttnResMaxBlocks || L < 1 || L > kda::kAttnResMaxLayers || T < 0) return 0;
+    return (size_t)n * (size_t)T * (16 + 1) * sizeof(float);
 }
 
 }  // extern "C"
@@ -158,6 +164,78 @@ kda_status_t kda_gate(kda_dtype_t io, int Ntok, int Dm, int H, int d_k, int r, c
     a.beta = beta;
     a.g = g;
     return kda::launch_gate(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the AttnRes entry points: dtype, sizes, the host array of block pointers.
+kda_status_t check_attnres(kda_dtype_t io, int n, int T, int d, float eps, const void *const *blocks) {
+    if (!valid_dtype(io) || n < 1 || T < 0 || d <= 0 || !(eps >= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+    if (io != KDA_BF16 || n > kda::kAttnResMaxBlocks || d % 512 != 0 || d > 4096) return KDA_ERR_UNSUPPORTED;
+    if (T == 0) return KDA_OK;
+    if (!blocks) return KDA_ERR_INVALID_ARGUMENT;
+    for (int b = 0; b < n; ++b)
+        if (!blocks[b] || !aligned16(blocks[b])) return KDA_ERR_INVALID_ARGUMENT;
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_attnres(kda_dtype_t io, int n, int T, int d, const void *const *blocks, const void *w, float eps,
+                         void *h, hipStream_t stream) {
+    kda_status_t st = check_attnres(io, n, T, d, eps, blocks);
+    if (st != KDA_OK || T == 0) return st;
+    if (!w || !h || !aligned16(w) || !aligned16(h)) return KDA_ERR_INVALID_ARGUMENT;
+    kda::AttnResArgs a{};
+    a.n = n; a.T = T; a.d = d; a.eps = eps;
+    for (int b = 0; b < n; ++b) a.blk[b] = static_cast<const uint16_t *>(blocks[b]);
+    a.w = static_cast<const uint16_t *>(w);
+    a.prior_o = nullptr; a.prior_lse = nullptr;
+    a.h = static_cast<uint16_t *>(h);
+    return kda::launch_attnres(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_attnres_inter(kda_dtype_t io, int n, int L, int T, int d, const void *const *blocks, const void *W,
+                               float eps, void *o_bar, float *lse, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (L < 1) return KDA_ERR_INVALID_ARGUMENT;
+    kda_status_t st = check_attnres(io, n, T, d, eps, blocks);
+    if (st != KDA_OK) return st;
+    if (L > kda::kAttnResMaxLayers) return KDA_ERR_UNSUPPORTED;
+    if (T == 0) return KDA_OK;
+    if (!W || !o_bar || !aligned16(W) || !aligned16(o_bar) || (lse && !aligned4(lse))) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t need = kda_attnres_inter_workspace_bytes(n, L, T);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace)) return KDA_ERR_WORKSPACE;
+    kda::AttnScoreArgs s{};
+    kda::AttnMixArgs m{};
+    s.n = m.n = n; s.L = m.L = L; s.T = m.T = T; s.d = m.d = d;
+    for (int b = 0; b < n; ++b) s.blk[b] = m.blk[b] = static_cast<const uint16_t *>(blocks[b]);
+    float *dots = static_cast<float *>(workspace);
+    float *sumsq = dots + (size_t)n * T * 16;
+    s.W = static_cast<const uint16_t *>(W); s.dots = dots; s.sumsq = sumsq;
+    m.eps = eps; m.dots = dots; m.sumsq = sumsq; m.o = static_cast<uint16_t *>(o_bar); m.lse = lse;
+    return kda::launch_attnres_inter(s, m, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_attnres_merge(kda_dtype_t io, int T, int d, const void *partial, const void *w, float eps,
+                               const void *o_bar, const float *lse, void *h, hipStream_t stream) {
+    const void *blocks[1] = {partial};
+    kda_status_t st = check_attnres(io, 1, T, d, eps, blocks);
+    if (st != KDA_OK || T == 0) return st;
+    if (!w || !o_bar || !lse || !h || !aligned16(w) || !aligned16(o_bar) || !aligned4(lse) || !aligned16(h))
+        return KDA_ERR_INVALID_ARGUMENT;
+    kda::AttnResArgs a{};
+    a.n = 1; a.T = T; a.d = d; a.eps = eps;
+    a.blk[0] = static_cast<const uint16_t *>(partial);
+    a.w = static_cast<const uint16_t *>(w);
+    a.prior_o = static_cast<const uint16_t *>(o_bar);
+    a.prior_lse = lse;
+    a.h = static_cast<uint16_t *>(h);
+    return kda::launch_attnres(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_fwd_chunk_local(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,

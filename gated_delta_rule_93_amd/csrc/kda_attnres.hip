@@ -1,0 +1,274 @@
+// kda_attnres.hip -- Block AttnRes read-out over stored block outputs (bf16 hidden states).
+//
+// For one layer with query w (blog post-114, chapter 6, the block AttnRes listing; page "Kimi K3
+// 注意力三件套", AttnRes section):  h[t] = sum_n softmax_n(w . norm(V_n[t])) V_n[t], where norm is an
+// RMS norm over the hidden width.  Two-phase inference (same page): for the L layers of a block
+// the stored blocks are scored and mixed once for all layers (phase 1: per layer the
+// softmax-weighted mean o and the log-sum-exp of the scores), then each layer merges its partial
+// block with an online-softmax step (phase 2).
+//
+// Kernels
+//   attnres_online_kernel  one wave per token: a single pass over the blocks with an online
+//                          softmax (running max, rescaled sum); serves the one-shot read-out and,
+//                          seeded with (o, lse), the phase-2 merge.
+//   attnres_scores_kernel  phase 1a: the scores' dot products w_l . V_n[t] and sum V_n[t]^2 as one
+//                          bf16 MFMA product over the width, rows = 16 tokens of one block.
+//   attnres_mix_kernel     phase 1b: per token, the softmax over the blocks for every layer and the
+//                          weighted sums o_l = sum_n a_ln V_n (the blocks are read once for all L).
+#include <utility>
+
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+__device__ __forceinline__ void unpack8(const u32x4 &w, float *x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+
+__device__ __forceinline__ u32x4 pack8(const float *x) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)x[2 * i]);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)x[2 * i + 1]);
+        r[i] = lo | (hi << 16);
+    }
+    return r;
+}
+
+// Sum over the 64 lanes of a wave (butterfly; every lane ends with the same value, in the same
+// order on every lane, so results are reproducible).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- one-shot read-out / merge
+// J = d / 512: lane l holds channels 512 j + 8 l .. + 7 of every row, j < J.
+template <int J>
+__global__ void __launch_bounds__(256) attnres_online_kernel(AttnResArgs a) {
+    const int lane = threadIdx.x & 63;
+    const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= a.T) return;  // whole wave
+    const float inv_d = 1.f / (float)(512 * J);
+    const long row = t * (512 * J) + 8 * lane;
+    u32x4 wq[J], xb[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        wq[j] = *reinterpret_cast<const u32x4 *>(a.w + 512 * j + 8 * lane);
+        xb[j] = *reinterpret_cast<const u32x4 *>(a.blk[0] + row + 512 * j);
+    }
+    float acc[J][8];
+    float m = -INFINITY, s = 0.f;
+    if (a.prior_o) {  // earlier blocks, summarised by their softmax-weighted mean and log-sum-exp
+        m = a.prior_lse[t];
+        s = 1.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) unpack8(*reinterpret_cast<const u32x4 *>(a.prior_o + row + 512 * j), acc[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] = 0.f;
+    }
+    for (int b = 0; b < a.n; ++b) {
+        float ss = 0.f, dw = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            float x[8], wf[8];
+            unpack8(xb[j], x);
+            unpack8(wq[j], wf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ss += x[i] * x[i];
+                dw += wf[i] * x[i];
+            }
+        }
+        u32x4 xn[J];  // next block's row, in flight while this one is folded in
+        const uint16_t *nb = a.blk[b + 1 < a.n ? b + 1 : b];
+#pragma unroll
+        for (int j = 0; j < J; ++j) xn[j] = *reinterpret_cast<const u32x4 *>(nb + row + 512 * j);
+        ss = wave_sum(ss);
+        dw = wave_sum(dw);
+        const float l = dw / sqrtf(ss * inv_d + a.eps);  // w . (x / rms(x))
+        const float mn = fmaxf(m, l);
+        const float c = fast_exp2((m - mn) * kLog2e), p = fast_exp2((l - mn) * kLog2e);
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            float x[8];
+            unpack8(xb[j], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] = acc[j][i] * c + p * x[i];
+            xb[j] = xn[j];
+        }
+        s = s * c + p;
+        m = mn;
+    }
+    const float inv_s = 1.f / s;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = acc[j][i] * inv_s;
+        *reinterpret_cast<u32x4 *>(a.h + row + 512 * j) = pack8(y);
+    }
+}
+
+// ---------------------------------------------------------------- phase 1a: score dot products
+// Wave (block b, 16 tokens): rows = tokens, columns = layers (<= 16), k = width in blocks of 32
+// with lane (grp, r16) holding the 8 consecutive width indices 32 kb + 8 grp .. (A and B alike).
+// A second MFMA of the tile with itself gives sum x^2 of each token row on its diagonal.
+__global__ void __launch_bounds__(256) attnres_scores_kernel(AttnScoreArgs a) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    const int b = blockIdx.y;
+    const long t0 = ((long)blockIdx.x * 4 + wave) * 16;
+    if (t0 >= a.T) return;  // whole wave
+    const long trow = t0 + r16 < a.T ? t0 + r16 : a.T - 1;
+    const uint16_t *xp = a.blk[b] + trow * a.d + 8 * grp;
+    const bool wvalid = r16 < a.L;
+    const uint16_t *wp = a.W + (long)(wvalid ? r16 : 0) * a.d + 8 * grp;
+    const int nkb = a.d / 32;
+    f32x4 dots = zero4(), sq = zero4();
+    for (int kb = 0; kb < nkb; kb += 4) {  // d is a multiple of 512: whole steps of four
+        u32x4 xv[4], wv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xv[i] = *reinterpret_cast<const u32x4 *>(xp + 32 * (kb + i));
+            wv[i] = *reinterpret_cast<const u32x4 *>(wp + 32 * (kb + i));
+        }
+        // all eight loads in flight before the MFMAs that use them
+        asm volatile("" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]),
+                          "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const FragB xa{__builtin_bit_cast(bf16x8, xv[i])};
+            const FragB wb{__builtin_bit_cast(bf16x8, wvalid ? wv[i] : u32x4{0u, 0u, 0u, 0u})};
+            dots = mfma(xa, wb, dots);
+            sq = mfma(xa, xa, sq);
+        }
+    }
+    // lane (grp, r16) holds rows 4 grp + e, column r16
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const long t = t0 + 4 * grp + e;
+        if (t >= a.T) continue;
+        if (r16 < a.L) a.dots[((long)b * a.T + t) * 16 + r16] = dots[e];
+        if (r16 == 4 * grp + e) a.sumsq[(long)b * a.T + t] = sq[e];
+    }
+}
+
+// ---------------------------------------------------------------- phase 1b: softmax and mix
+// One wave per token; NB = number of blocks.  Lane l < L forms layer l's softmax over the blocks
+// and its log-sum-exp; the weights go through LDS to every lane, which then mixes its 8-channel
+// slices of the blocks (loaded once per slice) for the layers, four at a time.
+template <int NB>
+__global__ void __launch_bounds__(256) attnres_mix_kernel(AttnMixArgs a) {
+    __shared__ float wts[4][kAttnResMaxLayers][NB];  // [wave][layer][block]
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long t = (long)blockIdx.x * 4 + wave;
+    if (t >= a.T) return;  // whole wave; no workgroup barrier below
+    const float inv_d = 1.f / (float)a.d;
+    if (lane < a.L) {
+        float lg[NB];
+        float m = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float ssq = a.sumsq[(long)b * a.T + t];
+            lg[b] = a.dots[((long)b * a.T + t) * 16 + lane] / sqrtf(ssq * inv_d + a.eps);
+            m = fmaxf(m, lg[b]);
+        }
+        float sum = 0.f;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            lg[b] = fast_exp2((lg[b] - m) * kLog2e);
+            sum += lg[b];
+        }
+        const float inv = 1.f / sum;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wts[wave][lane][b] = lg[b] * inv;
+        if (a.lse) a.lse[(long)lane * a.T + t] = m + __builtin_amdgcn_logf(sum) * kLn2;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int J = a.d / 512;
+    for (int j = 0; j < J; ++j) {
+        const long off = t * a.d + 512 * j + 8 * lane;
+        u32x4 xb[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) xb[b] = *reinterpret_cast<const u32x4 *>(a.blk[b] + off);
+        for (int l0 = 0; l0 < a.L; l0 += 4) {
+            float acc[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                float x[8];
+                unpack8(xb[b], x);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float wl = wts[wave][(l0 + u) & (kAttnResMaxLayers - 1)][b];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[u][i] += wl * x[i];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (l0 + u < a.L) *reinterpret_cast<u32x4 *>(a.o + (long)(l0 + u) * a.T * a.d + off) = pack8(acc[u]);
+        }
+    }
+}
+
+hipError_t launch_attnres(const AttnResArgs &a, hipStream_t st) {
+    if (a.T <= 0) return hipSuccess;
+    const dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
+    switch (a.d / 512) {
+        case 1: hipLaunchKernelGGL(attnres_online_kernel<1>, grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL(attnres_online_kernel<2>, grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL(attnres_online_kernel<3>, grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL(attnres_online_kernel<4>, grid, block, 0, st, a); break;
+        case 5: hipLaunchKernelGGL(attnres_online_kernel<5>, grid, block, 0, st, a); break;
+        case 6: hipLaunchKernelGGL(attnres_online_kernel<6>, grid, block, 0, st, a); break;
+        case 7: hipLaunchKernelGGL(attnres_online_kernel<7>, grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL(attnres_online_kernel<8>, grid, block, 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int NB>
+static void launch_mix(const AttnMixArgs &m, hipStream_t st) {
+    hipLaunchKernelGGL(attnres_mix_kernel<NB>, dim3((unsigned)((m.T + 3) / 4)), dim3(256), 0, st, m);
+}
+
+template <int... NBs>
+static bool launch_mix_n(const AttnMixArgs &m, hipStream_t st, std::integer_sequence<int, NBs...>) {
+    bool done = false;
+    ((m.n == NBs + 1 ? (launch_mix<NBs + 1>(m, st), done = true) : false), ...);
+    return done;
+}
+
+hipError_t launch_attnres_inter(const AttnScoreArgs &s, const AttnMixArgs &m, hipStream_t st) {
+    if (s.T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(attnres_scores_kernel, dim3((unsigned)((s.T + 63) / 64), (unsigned)s.n), dim3(256), 0, st, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (!launch_mix_n(m, st, std::make_integer_sequence<int, kAttnResMaxBlocks>{})) return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace kda

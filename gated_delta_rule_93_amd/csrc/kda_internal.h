@@ -63,4 +63,32 @@ struct GateArgs {
 };
 hipError_t launch_gate(const GateArgs &a, hipStream_t st);
 
+constexpr int kAttnResMaxBlocks = 16, kAttnResMaxLayers = 16;
+struct AttnResArgs {             // one-shot read-out, or the merge when prior_o != NULL
+    int n, T, d;
+    const uint16_t *blk[kAttnResMaxBlocks];  // block outputs, each [T, d] bf16
+    const uint16_t *w;                       // [d] bf16 query
+    float eps;
+    const uint16_t *prior_o;                 // [T, d] bf16 or NULL
+    const float *prior_lse;                  // [T] (with prior_o)
+    uint16_t *h;                             // [T, d] bf16
+};
+struct AttnScoreArgs {
+    int n, L, T, d;
+    const uint16_t *blk[kAttnResMaxBlocks];
+    const uint16_t *W;                       // [L, d] bf16 queries
+    float *dots;                             // [n, T, 16] workspace
+    float *sumsq;                            // [n, T] workspace
+};
+struct AttnMixArgs {
+    int n, L, T, d;
+    const uint16_t *blk[kAttnResMaxBlocks];
+    float eps;
+    const float *dots, *sumsq;
+    uint16_t *o;                             // [L, T, d] bf16
+    float *lse;                              // [L, T] or NULL
+};
+hipError_t launch_attnres(const AttnResArgs &a, hipStream_t st);
+hipError_t launch_attnres_inter(const AttnScoreArgs &s, const AttnMixArgs &m, hipStream_t st);
+
 }  // namespace kda

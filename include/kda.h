@@ -185,6 +185,53 @@ kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, 
                                   hipStream_t stream);
 
 /*
+ * Block AttnRes.  Blog post-114, chapter 6 (the block AttnRes listing): the outputs of the
+ * earlier blocks of layers (and the current, partial block) are stacked, normalised into keys,
+ * scored against the layer's projection weight w, and mixed with the softmax of the scores over
+ * the blocks; the page "Kimi K3 注意力三件套" (AttnRes section) adds that the weights sum to one,
+ * and that at inference the scoring of the stored blocks is done once for all layers of a block
+ * (phase 1), each layer then merging its partial block by an online-softmax step (phase 2):
+ *     h[t] = sum_n softmax_n( w . norm(V_n[t]) ) V_n[t],   norm(x) = x / sqrt(mean(x^2) + eps)
+ * (an RMS norm without learned scale: a scale would only multiply w element-wise).
+ * Block outputs, queries and results are bf16 ([T, d] each, row-major); arithmetic is fp32.
+ * `blocks` is a HOST array of n device pointers.  Device buffers are 16-byte aligned, except the
+ * fp32 lse arrays (4-byte aligned, so a layer's row of a [L, T] array can be passed).  Supported: n <= 16 blocks, L <= 16 layers,
+ * d a multiple of 512 up to 4096; io = KDA_BF16 only.  eps >= 0.
+ */
+
+/*
+ * kda_attnres -- one-shot read-out of one layer over n blocks (the last may be the partial
+ * block): h [T, d].  h may alias one of the blocks (each element is read before it is written).
+ */
+kda_status_t kda_attnres(kda_dtype_t io, int n, int T, int d, const void *const *blocks,
+                         const void *w, float eps, void *h, hipStream_t stream);
+
+/*
+ * kda_attnres_inter -- phase 1 for L layers over n stored blocks, each block read once:
+ *   o_bar  [L, T, d] bf16 out: per layer the softmax-weighted mean over the blocks
+ *   lse    [L, T] fp32 out or NULL: per layer the log-sum-exp of the scores
+ *   W      [L, d] bf16: the layers' queries
+ *   workspace: device, kda_attnres_inter_workspace_bytes(n, L, T) bytes, caller-owned.
+ * o_bar must not overlap the blocks.
+ */
+size_t kda_attnres_inter_workspace_bytes(int n, int L, int T);
+kda_status_t kda_attnres_inter(kda_dtype_t io, int n, int L, int T, int d, const void *const *blocks,
+                               const void *W, float eps, void *o_bar, float *lse,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_attnres_merge -- phase 2 for one layer: merges the partial block [T, d] into that layer's
+ * phase-1 result (o_bar [T, d], lse [T]: one layer's slices of kda_attnres_inter's outputs):
+ *     m = max(lse, s),  s = w . norm(partial),
+ *     h = (e^{lse-m} o_bar + e^{s-m} partial) / (e^{lse-m} + e^{s-m}),
+ * equal to kda_attnres over the stored blocks and the partial block.  lse = -inf (no stored
+ * block) gives h = partial.  h may alias partial or o_bar.
+ */
+kda_status_t kda_attnres_merge(kda_dtype_t io, int T, int d, const void *partial, const void *w,
+                               float eps, const void *o_bar, const float *lse, void *h,
+                               hipStream_t stream);
+
+/*
  * kda_decode_step -- one token of the recurrence for N independent sequences, in place.
  * The state stays resident in HBM; each call reads and rewrites it once
  * (the fixed-size state of the course page's section 2 makes each step O(1) in the

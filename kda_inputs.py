@@ -391,3 +391,18 @@ def make_lowrank(B: int, T: int, H: int, d: int, r: int, seed: int, s0_std: Opti
     S0 = None if s0_std is None else rng.standard_normal((N, H, d, d), dtype=np.float32) * np.float32(s0_std)
     _, _, w_up, b = gate_weights(H * d, H, d, r, seed, b_mean=b_mean)
     return LowRankInputs(bf16_round(q), bf16_round(k), bf16_round(v), beta, bf16_round(z), w_up, b, S0, cu)
+
+
+# --------------------------------------------------------------------------- Block AttnRes inputs
+def attnres_inputs(n: int, T: int, d: int, L: int, seed: int, score_std: float = 1.5):
+    """Block outputs V [n, T, d] (bf16 values in fp32 storage; block b ~ N(0, (1 + b/2)^2), so the
+    blocks differ in scale as residual streams grow with depth) and L layer queries W [L, d]
+    ~ N(0, score_std^2 / d) (bf16 values), so that w . norm(V) ~ N(0, score_std^2).
+    Draw order: V (block by block), W."""
+    rng = np.random.default_rng([seed, 3])
+    V = np.empty((n, T, d), np.float32)
+    for b in range(n):
+        V[b] = rng.standard_normal((T, d), dtype=np.float32) * np.float32(1.0 + 0.5 * b)
+    _store_bf16_inplace(V)
+    W = bf16_round(rng.standard_normal((L, d), dtype=np.float32) * np.float32(score_std / np.sqrt(d)))
+    return V, W

@@ -11,6 +11,9 @@ Contents
   gate_z, gate_g, gate_beta, gate
                   low-rank gate: z = x W_down^T, log(alpha) = -softplus(z W_up^T + b),
                   beta = sigmoid(x w_beta^T) (numpy fp64).
+  attnres, attnres_logits, attnres_lse, rms_norm
+                  Block AttnRes read-out: softmax over the blocks of w . norm(V_n), then the
+                  weighted sum of the blocks V_n (numpy fp64).
 
 Sources (the pages this follows)
   * Course page "线性注意力与 KDA" (ai.air7.fun, Day 19), section 3: the decay
@@ -24,7 +27,12 @@ Sources (the pages this follows)
     chapter 4 (per-channel alpha multiplies the state rows; alpha = gate(x) is
     computed from the input, per layer, head and channel).
   * Page "Kimi K3 注意力三件套", KDA section: alpha comes from a low-rank
-    down-up projection of the input; beta is a single scalar.
+    down-up projection of the input; beta is a single scalar.  AttnRes section:
+    softmax weights over the earlier blocks' outputs, summing to one; two-phase
+    inference with an online-softmax merge.
+  * Blog post-114, chapter 6: the block AttnRes listing (stack the block outputs,
+    normalise them as keys, score them with the layer's projection weight, softmax
+    over the blocks, weighted sum).
 
 Readings adopted where the pages are silent (each also listed in the design doc):
   state K-major [d_k, d_v] with o = S^T q; decay before the delta read; read-out
@@ -32,7 +40,9 @@ Readings adopted where the pages are silent (each also listed in the design doc):
   head; prologue = conv (width W, zero history at each sequence start, last tap
   on the current token, no bias) -> SiLU -> x / max(||x||_2, 1e-12) per head;
   gate: log(alpha) = -softplus(up(down(x)) + b) with a per-channel bias b and no
-  bias inside the projections, beta = sigmoid(w_beta . x) without bias.
+  bias inside the projections, beta = sigmoid(w_beta . x) without bias; AttnRes:
+  the "norm" of the listing is an RMS norm over the hidden width with an epsilon
+  argument and no learned scale.
 """
 from __future__ import annotations
 
@@ -279,3 +289,40 @@ def gate(x, w_down, w_beta, w_up, b, H: int, d: int):
     unrounded z."""
     z = gate_z(x, w_down)
     return z, gate_beta(x, w_beta), gate_g(z, w_up, b, H, d)
+
+
+# --------------------------------------------------------------------------- Block AttnRes
+def rms_norm(x: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2 over the last axis) + eps), fp64, without a learned scale (a scale
+    would multiply the query vector w element-wise, so it is folded into w)."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def attnres_logits(V: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """Scores of the stored block outputs for one layer's query w: logits[n, t] = w . norm(V[n, t]).
+
+    V [n, T, d] (the blocks' outputs for each token, the last one possibly the partial block),
+    w [d].  Blog post-114, chapter 6 (the block AttnRes listing): the stacked block outputs are
+    normalised to form the keys and scored against the layer's projection weight."""
+    return np.einsum("ntd,d->nt", rms_norm(V, eps), np.asarray(w, np.float64))
+
+
+def attnres(V: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """Block AttnRes read-out for one layer, fp64: h[t] = sum_n softmax_n(logits[:, t]) V[n, t].
+
+    Blog post-114, chapter 6 (softmax of the scores over the blocks, then the weighted sum of
+    the blocks); page "Kimi K3 注意力三件套" (AttnRes section: the weights over the blocks sum to
+    one and depend on the input).  Returns [T, d]."""
+    lg = attnres_logits(V, w, eps)
+    a = np.exp(lg - lg.max(axis=0, keepdims=True))
+    a /= a.sum(axis=0, keepdims=True)
+    return np.einsum("nt,ntd->td", a, np.asarray(V, np.float64))
+
+
+def attnres_lse(V: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """log sum_n exp(logits[n, t]) over the blocks, [T]: with attnres() the partial result that
+    the two-phase inference of the yeyulingfeng page keeps for the online-softmax merge."""
+    lg = attnres_logits(V, w, eps)
+    m = lg.max(axis=0)
+    return m + np.log(np.exp(lg - m[None, :]).sum(axis=0))

@@ -193,3 +193,51 @@ def test_gate_empty_and_g_optional():
     assert gate_call(Ntok=0) == kda.KDA_OK
     assert gate_call(Ntok=0, g=None, w_up=None, b=None) == kda.KDA_OK
     assert lowrank_call(H=0, ws=None, wsb=0) == kda.KDA_OK
+
+
+def attnres_call(n=3, T=10, d=512, eps=1e-6, blocks="ok", w=FAKE, h=FAKE):
+    if blocks == "ok":
+        blocks = [FAKE + 4096 * i for i in range(n)]
+    arr = None if blocks is None else (ctypes.c_void_p * max(len(blocks), 1))(*blocks)
+    return kda.lib().kda_attnres(kda.KDA_BF16, n, T, d, arr, w, eps, h, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(eps=-1.0), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(eps=float("nan")), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(blocks=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(blocks=[FAKE, None, FAKE]), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(blocks=[FAKE, FAKE + 8, FAKE]), kda.KDA_ERR_INVALID_ARGUMENT),   # misaligned block
+    (dict(w=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(h=FAKE + 2), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(n=17, blocks=[FAKE] * 17), kda.KDA_ERR_UNSUPPORTED),
+    (dict(d=768), kda.KDA_ERR_UNSUPPORTED),                               # not a multiple of 512
+    (dict(d=4608), kda.KDA_ERR_UNSUPPORTED),                              # above 4096
+])
+def test_attnres_rejects(kw, code):
+    assert attnres_call(**kw) == code
+
+
+def test_attnres_other_entries_reject_and_accept_empty():
+    L = kda.lib()
+    arr = (ctypes.c_void_p * 2)(FAKE, FAKE + 4096)
+    assert L.kda_attnres(kda.KDA_F32, 2, 10, 512, arr, FAKE, 1e-6, FAKE, None) == kda.KDA_ERR_UNSUPPORTED
+    assert attnres_call(T=0, blocks=None, w=None, h=None) == kda.KDA_OK
+    need = L.kda_attnres_inter_workspace_bytes(2, 12, 100)
+    assert need == 2 * 100 * 17 * 4
+    assert L.kda_attnres_inter_workspace_bytes(0, 12, 100) == 0
+    assert L.kda_attnres_inter(kda.KDA_BF16, 2, 0, 100, 512, arr, FAKE, 1e-6, FAKE, FAKE, FAKE, need, None) \
+        == kda.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_attnres_inter(kda.KDA_BF16, 2, 17, 100, 512, arr, FAKE, 1e-6, FAKE, FAKE, FAKE, need, None) \
+        == kda.KDA_ERR_UNSUPPORTED
+    assert L.kda_attnres_inter(kda.KDA_BF16, 2, 12, 100, 512, arr, FAKE, 1e-6, FAKE, FAKE, FAKE, need - 4, None) \
+        == kda.KDA_ERR_WORKSPACE
+    assert L.kda_attnres_inter(kda.KDA_BF16, 2, 12, 100, 512, arr, None, 1e-6, FAKE, FAKE, FAKE, need, None) \
+        == kda.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_attnres_merge(kda.KDA_BF16, 10, 512, FAKE, FAKE, 1e-6, FAKE, None, FAKE, None) \
+        == kda.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_attnres_merge(kda.KDA_BF16, 10, 640, FAKE, FAKE, 1e-6, FAKE, FAKE, FAKE, None) \
+        == kda.KDA_ERR_UNSUPPORTED
+    assert L.kda_attnres_merge(kda.KDA_BF16, 0, 512, None, None, 1e-6, None, None, None, None) == kda.KDA_OK
