@@ -13,7 +13,7 @@ The same run also measures
   * the fp64 CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel times come from HIP events recorded on the stream the kernels run on.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,scalar,gate,long,varlen,cpu,copy]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,scalar,gate,attnres,long,varlen,cpu,copy]
 Prints one JSON line.  `--only copy` runs a plain 256 MiB device copy (a kernel of known size
 used to calibrate the FETCH_SIZE / WRITE_SIZE counters of profiler runs).
 The roofline "traffic" figure comes from profiles/traffic.json (counter runs of this same
@@ -22,6 +22,7 @@ script); it is reported only while the hash of the kernel source recorded there 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -327,6 +328,51 @@ def bench_lowrank_gate(torch, kda, dev, reps=20):
     return out
 
 
+def bench_attnres(torch, kda, dev, reps=20):
+    """Block AttnRes over 16,384 tokens of width 2048 (the prefill batch's tokens, width H*d):
+    8 blocks (7 stored + the partial one) and 12 layers per block.  Times the one-shot read-out of
+    one layer over the 8 blocks, phase 1 of the two-phase inference (the 7 stored blocks scored and
+    mixed for all 12 layers), and one layer's phase-2 merge; a block's total either way."""
+    T, d, n, L, eps = 16384, 2048, 8, 12, 1e-6
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93350)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    blocks = [(rnd(T, d) * (1.0 + 0.5 * b)).to(torch.bfloat16) for b in range(n)]
+    W = (rnd(L, d) * (1.5 / d ** 0.5)).to(torch.bfloat16)
+    o = torch.empty((L, T, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((L, T), dtype=torch.float32, device=dev)
+    h = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    L_ = kda.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    arr_all = (ctypes.c_void_p * n)(*[b.data_ptr() for b in blocks])
+    arr_hist = (ctypes.c_void_p * (n - 1))(*[b.data_ptr() for b in blocks[:-1]])
+    nws = int(L_.kda_attnres_inter_workspace_bytes(n - 1, L, T))
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    one = lambda: L_.kda_attnres(kda.KDA_BF16, n, T, d, arr_all, W.data_ptr(), eps, h.data_ptr(), st)
+    inter = lambda: L_.kda_attnres_inter(kda.KDA_BF16, n - 1, L, T, d, arr_hist, W.data_ptr(), eps, o.data_ptr(),
+                                         lse.data_ptr(), ws.data_ptr(), nws, st)
+    merge = lambda: L_.kda_attnres_merge(kda.KDA_BF16, T, d, blocks[-1].data_ptr(), W.data_ptr(), eps,
+                                         o.data_ptr(), lse.data_ptr(), h.data_ptr(), st)
+    out = {"workload": "Block AttnRes, 16384 tokens, width 2048, bf16: 8 blocks (7 stored + partial), "
+                       "12 layers per block"}
+    for label, fn in (("one_shot_layer", one), ("phase1_all_layers", inter), ("phase2_merge_layer", merge)):
+        for _ in range(3):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        out[label + "_ms"] = time_events(lambda: fn(), reps, torch)
+    row = T * d * 2
+    one_b, p1_b, p2_b = (n + 1) * row, (n - 1) * row + L * row + L * T * 4, 3 * row + T * 4
+    out["one_shot_layer_GBs"] = one_b / out["one_shot_layer_ms"] / 1e6
+    out["one_shot_layer_hbm_frac"] = out["one_shot_layer_GBs"] / HBM_PEAK_GBS
+    out["phase1_algorithmic_GBs"] = p1_b / out["phase1_all_layers_ms"] / 1e6
+    out["phase1_hbm_frac"] = out["phase1_algorithmic_GBs"] / HBM_PEAK_GBS
+    out["phase2_merge_GBs"] = p2_b / out["phase2_merge_layer_ms"] / 1e6
+    out["phase2_hbm_frac"] = out["phase2_merge_GBs"] / HBM_PEAK_GBS
+    out["block_one_shot_ms"] = L * out["one_shot_layer_ms"]
+    out["block_two_phase_ms"] = out["phase1_all_layers_ms"] + L * out["phase2_merge_layer_ms"]
+    return out
+
+
 def bench_varlen_layer(torch, kda, dev, reps=5):
     """Varlen layer: 64 packed sequences (lengths U[512, 16384] from the workload seed), H=32, d=128:
     prologue on raw q and k (width 4), then the chunked prefill with per-sequence S_0 ~ N(0, 0.02)."""
@@ -434,8 +480,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,long,varlen,cpu",
-                    help="comma list of prefill, decode, prep, scalar, gate, long, varlen, cpu, copy")
+    ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,attnres,long,varlen,cpu",
+                    help="comma list of prefill, decode, prep, scalar, gate, attnres, long, varlen, cpu, copy")
     args = ap.parse_args()
     only = set(x.strip() for x in args.only.split(",") if x.strip())
     if args.gpus != 1:
@@ -457,6 +503,8 @@ def main():
             out["scalar_gate"] = bench_scalar_gate(torch, kda, dev)
         if "gate" in only:
             out["lowrank_gate"] = bench_lowrank_gate(torch, kda, dev)
+        if "attnres" in only:
+            out["attnres"] = bench_attnres(torch, kda, dev)
         if "long" in only:
             out["long_context"] = bench_long(torch, kda, dev)
         if "varlen" in only:
@@ -523,6 +571,9 @@ def main():
     if "gate" in only:
         log("low-rank gate ...")
         out["lowrank_gate"] = bench_lowrank_gate(torch, kda, dev)
+    if "attnres" in only:
+        log("block attnres ...")
+        out["attnres"] = bench_attnres(torch, kda, dev)
     if "long" in only:
         log("long context ...")
         out["long_context"] = bench_long(torch, kda, dev)
