@@ -141,18 +141,19 @@ __global__ void __launch_bounds__(256) attnres_scores_kernel(AttnScoreArgs a) {
     const uint16_t *wp = a.W + (long)(wvalid ? r16 : 0) * a.d + 8 * grp;
     const int nkb = a.d / 32;
     f32x4 dots = zero4(), sq = zero4();
-    for (int kb = 0; kb < nkb; kb += 4) {  // d is a multiple of 512: whole steps of four
-        u32x4 xv[4], wv[4];
+    for (int kb = 0; kb < nkb; kb += 8) {  // d is a multiple of 512: whole steps of eight
+        u32x4 xv[8], wv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             xv[i] = *reinterpret_cast<const u32x4 *>(xp + 32 * (kb + i));
             wv[i] = *reinterpret_cast<const u32x4 *>(wp + 32 * (kb + i));
         }
-        // all eight loads in flight before the MFMAs that use them
-        asm volatile("" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]),
-                          "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]));
+        // all sixteen loads in flight before the MFMAs that use them
+        asm volatile("" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]),
+                          "+v"(xv[6]), "+v"(xv[7]), "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]),
+                          "+v"(wv[4]), "+v"(wv[5]), "+v"(wv[6]), "+v"(wv[7]));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 8; ++i) {
             const FragB xa{__builtin_bit_cast(bf16x8, xv[i])};
             const FragB wb{__builtin_bit_cast(bf16x8, wvalid ? wv[i] : u32x4{0u, 0u, 0u, 0u})};
             dots = mfma(xa, wb, dots);
