@@ -9,7 +9,9 @@
 // HBM-bound stencil.  Each thread owns 8 consecutive channels (one 16-byte bf16 vector) of one
 // head and walks TT consecutive tokens, keeping the W-1 previous inputs in registers, so the
 // input is read once plus a (W-1)/TT halo.  The d/8 lanes of a head reduce the sum of squares
-// with xor shuffles inside their aligned lane group (fixed order, deterministic).
+// with xor shuffles inside their aligned lane group (fixed order, deterministic).  SiLU and the
+// norm use the hardware reciprocal and reciprocal square root (about 1 ulp each): the division
+// and square root of IEEE fp32 made the kernel issue-bound at 3.7 TB/s.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -130,13 +132,13 @@ prep_kernel(const TIO *__restrict__ x, const float *__restrict__ w, TIO *__restr
             float c = wt[j][W - 1] * xc[j];
 #pragma unroll
             for (int m = 0; m < W - 1; ++m) c = fmaf(wt[j][m], hist[m][j], c);
-            const float s = c / (1.f + __expf(-c));
+            const float s = c * __builtin_amdgcn_rcpf(1.f + fast_exp2(-c * kLog2e));
             yv[j] = s;
             ss = fmaf(s, s, ss);
         }
 #pragma unroll
         for (int off = LPH / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-        const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+        const float inv = ss > 1e-24f ? __builtin_amdgcn_rsqf(ss) : 1e12f;  // 1 / max(||y||, 1e-12)
 #pragma unroll
         for (int j = 0; j < 8; ++j) yv[j] *= inv;
         if (active) Vec8<TIO>::store(y + t * row + c0, yv);

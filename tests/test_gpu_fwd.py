@@ -121,3 +121,35 @@ def test_prefill_equals_decode_steps():
     o_dec = torch.stack(outs, dim=1)
     assert err(host(o_pf), host(o_dec), "f32") <= tol("f32")
     assert err(host(S_pf), host(st), "f32") <= tol("f32")
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_fwd_beta_zero_alpha_one_keeps_state(io):
+    """beta = 0 and alpha = 1 (g = 0): the state never changes and o_t = scale S_0^T q_t, a closed
+    form (course page, section 3: nothing is written when beta = 0; no decay when alpha = 1)."""
+    inp = ki.make_dense(2, 150, 2, 64, 64, io, 61, s0_std=0.5)
+    inp.g[:] = 0.0
+    inp.beta[:] = 0.0
+    q, k, v, g, beta, S0, cu = upload(inp)
+    o, S = kda.fwd(q, k, v, g, beta, 0.75, S0, cu)
+    torch.cuda.synchronize()
+    o_ref = 0.75 * np.einsum("bthi,bhij->bthj", inp.q.astype(np.float64), inp.S0.astype(np.float64))
+    e_o, e_s = err(host(o), o_ref, io), err(host(S), inp.S0, io)
+    print(f"fwd beta=0 alpha=1 {io}: o err {e_o:.3e}, state err {e_s:.3e}")
+    assert e_o <= tol(io) and e_s <= 1e-6
+
+
+def test_fwd_packed_equals_per_sequence():
+    """A packed batch of three sequences gives, bitwise, what each sequence gives alone (chunks
+    restart at every sequence start, so every chunk and scan step sees the same operands)."""
+    inp = ki.make_varlen([150, 64, 333], 2, 128, 128, "bf16", 62, s0_std=0.3)
+    q, k, v, g, beta, S0, cu = upload(inp)
+    o, S = kda.fwd(q, k, v, g, beta, 1.0, S0, cu)
+    torch.cuda.synchronize()
+    for n in range(3):
+        s, e = int(inp.cu_seqlens[n]), int(inp.cu_seqlens[n + 1])
+        o1, S1 = kda.fwd(q[:, s:e].contiguous(), k[:, s:e].contiguous(), v[:, s:e].contiguous(),
+                         g[:, s:e].contiguous(), beta[:, s:e].contiguous(), 1.0, S0[n:n + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o[:, s:e]), n
+        assert torch.equal(S1, S[n:n + 1]), n
