@@ -11,7 +11,8 @@
 // input is read once plus a (W-1)/TT halo.  The d/8 lanes of a head reduce the sum of squares
 // with xor shuffles inside their aligned lane group (fixed order, deterministic).  SiLU and the
 // norm use the hardware reciprocal and reciprocal square root (about 1 ulp each): the division
-// and square root of IEEE fp32 made the kernel issue-bound at 3.7 TB/s.
+// and square root of IEEE fp32 made the kernel issue-bound at 3.7 TB/s.  bf16 rows are read and
+// written with non-temporal accesses (each byte is touched once here).
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -22,7 +23,8 @@ constexpr int kPrepTT = 32;
 template <typename TIO> struct Vec8;
 template <> struct Vec8<uint16_t> {
     static __device__ __forceinline__ void load(const uint16_t *p, float *x) {
-        uint4 w = *reinterpret_cast<const uint4 *>(p);
+        typedef __attribute__((ext_vector_type(4))) unsigned int v4u;
+        const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
         uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -31,12 +33,13 @@ template <> struct Vec8<uint16_t> {
         }
     }
     static __device__ __forceinline__ void store(uint16_t *p, const float *x) {
-        uint4 w;
+        typedef __attribute__((ext_vector_type(4))) unsigned int v4u;
+        v4u w;
         w.x = pack_bf16x2(x[0], x[1]);
         w.y = pack_bf16x2(x[2], x[3]);
         w.z = pack_bf16x2(x[4], x[5]);
         w.w = pack_bf16x2(x[6], x[7]);
-        *reinterpret_cast<uint4 *>(p) = w;
+        __builtin_nontemporal_store(w, reinterpret_cast<v4u *>(p));
     }
 };
 template <> struct Vec8<float> {
