@@ -395,6 +395,27 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     const int rg = tid / SM::CQ, c4 = (tid % SM::CQ) * 4;
     f32x4 gv[RPG];
     Raw4<TIO> kv[RPG], qv[RPG], vv[RPG];
+    // Low-rank gate: wave w forms the 16x16 tiles (tt, ct) of g for ct = w, w + 4, ... with
+    // A = z rows (tokens), B = W_up rows h*D + channel, k = rank index.  The operands of the
+    // first 32 rank indices are loaded before q, k, v, so the MFMAs and the nonlinearity below
+    // wait only for them and run while the q, k, v loads are still in flight.
+    constexpr int NCTW = (D / 16 + 3) / 4;  // column tiles per wave (low-rank gate)
+    FragB za[4], wb[NCTW];  // (unused, and removed by the compiler, when !LR)
+    auto load_gate_ops = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            const int t = 16 * tt + r16;
+            const uint16_t *zr = lr.z + (pos.tok0 + (t < Cc ? t : 0)) * (long)lr.r + 32 * kb + 4 * grp;
+            za[tt] = frag_bits(*reinterpret_cast<const uint2 *>(zr), *reinterpret_cast<const uint2 *>(zr + 16));
+        }
+#pragma unroll
+        for (int u = 0; u < NCTW; ++u) {
+            const int c = 16 * (wave + 4 * u) + r16;
+            const uint16_t *wr = lr.w_up + ((long)h * D + c) * lr.r + 32 * kb + 4 * grp;
+            wb[u] = frag_bits(*reinterpret_cast<const uint2 *>(wr), *reinterpret_cast<const uint2 *>(wr + 16));
+        }
+    };
+    if constexpr (LR) load_gate_ops(0);
     // Rows past the end of a partial chunk read row 0 instead (always valid) and are zeroed
     // afterwards, so every load is unconditional and all of them are in flight together.
 #pragma unroll
@@ -407,31 +428,16 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
         vv[r] = Raw4<TIO>::load(v + off);
     }
     if constexpr (LR) {
-        // g of this chunk and head (after the q, k, v loads above are in flight): wave w forms
-        // the 16x16 tiles (tt, ct) for ct = w, w + 4, ... with A = z rows (tokens), B = W_up rows
-        // h*D + channel, k = rank index; rows past a partial chunk's end are zero.  The tiles go to the G array of LDS, which the
-        // cumulative sum below then reads in its own layout.
+        // g of this chunk and head; rows past a partial chunk's end are zero.  The tiles go to the
+        // G array of LDS, which the cumulative sum below then reads in its own layout.
         static_assert(BF16, "the low-rank gate takes bf16 operands");
-        constexpr int NCTW = (D / 16 + 3) / 4;  // column tiles per wave
         f32x4 acc[4][NCTW];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int u = 0; u < NCTW; ++u) acc[tt][u] = zero4();
         for (int kb = 0; kb < lr.r / 32; ++kb) {
-            FragB za[4], wb[NCTW];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                const int t = 16 * tt + r16;
-                const uint16_t *zr = lr.z + (pos.tok0 + (t < Cc ? t : 0)) * (long)lr.r + 32 * kb + 4 * grp;
-                za[tt] = frag_bits(*reinterpret_cast<const uint2 *>(zr), *reinterpret_cast<const uint2 *>(zr + 16));
-            }
-#pragma unroll
-            for (int u = 0; u < NCTW; ++u) {
-                const int c = 16 * (wave + 4 * u) + r16;
-                const uint16_t *wr = lr.w_up + ((long)h * D + c) * lr.r + 32 * kb + 4 * grp;
-                wb[u] = frag_bits(*reinterpret_cast<const uint2 *>(wr), *reinterpret_cast<const uint2 *>(wr + 16));
-            }
+            if (kb > 0) load_gate_ops(kb);
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
