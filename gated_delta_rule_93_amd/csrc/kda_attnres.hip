@@ -200,6 +200,9 @@ __global__ void __launch_bounds__(256) attnres_mix_kernel(AttnMixArgs a) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) wts[wave][lane][b] = lg[b] * inv;
         if (a.lse) a.lse[(long)lane * a.T + t] = m + __builtin_amdgcn_logf(sum) * kLn2;
+    } else if (lane < kAttnResMaxLayers) {  // layers past L: zero weights (read, never stored)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wts[wave][lane][b] = 0.f;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -222,7 +225,7 @@ __global__ void __launch_bounds__(256) attnres_mix_kernel(AttnMixArgs a) {
                 unpack8(xb[b], x);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float wl = wts[wave][(l0 + u) & (kAttnResMaxLayers - 1)][b];
+                    const float wl = wts[wave][(l0 + u) & (kAttnResMaxLayers - 1)][b];  // l0 + u < 16
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[u][i] += wl * x[i];
                 }

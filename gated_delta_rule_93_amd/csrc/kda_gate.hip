@@ -50,15 +50,15 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
     // the unrolled iterations keep their loads in flight together.
     const uint16_t *xp = a.x + (long)xrow * a.Dm + 8 * grp;
     for (int cg = 0; cg < nct; cg += 4) {
-        const uint16_t *wp[4];
-        bool wv[4];
+        const uint16_t *wp[4];  // this lane's weight row of each tile of the group
+        bool wvalid[4];         // false for rows past H (and tiles past the last): zero operand
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int ct = cg + u;
             const bool zt = ct < nzt;
             const int row = zt ? 16 * ct + r16 : 16 * (ct - nzt) + r16;
-            wv[u] = zt || (ct < nct && row < a.H);
-            wp[u] = (wv[u] ? (zt ? a.w_down : a.w_beta) + (long)row * a.Dm : a.w_down) + 8 * grp;
+            wvalid[u] = zt || (ct < nct && row < a.H);
+            wp[u] = (wvalid[u] ? (zt ? a.w_down : a.w_beta) + (long)row * a.Dm : a.w_down) + 8 * grp;
         }
         f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
         // four k blocks per step: all 20 loads are issued before the 16 MFMAs that use them
@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
                 const FragB xa{__builtin_bit_cast(bf16x8, xv[i])};
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const u32x4 w = wv[u] ? wv4[i][u] : u32x4{0u, 0u, 0u, 0u};
+                    const u32x4 w = wvalid[u] ? wv4[i][u] : u32x4{0u, 0u, 0u, 0u};
                     acc[u] = mfma(xa, FragB{__builtin_bit_cast(bf16x8, w)}, acc[u]);
                 }
             }
