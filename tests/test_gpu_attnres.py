@@ -80,3 +80,28 @@ def test_attnres_two_phase_matches_one_shot_on_gpu():
         worst = max(worst, floored_rel(h2, h1))
     print(f"attnres two-phase vs one-shot on the GPU: {worst:.3e}")
     assert worst <= tol("bf16")
+
+
+def test_attnres_output_may_alias_a_block():
+    """h may be one of the input blocks (each element is read before it is written)."""
+    V, W = ki.attnres_inputs(4, 300, 1024, 1, 93360)
+    bl = blocks_dev(V)
+    wd = dev_io(W[0], "bf16")
+    ref = kda.attnres(bl, wd, EPS).clone()
+    kda.attnres(bl, wd, EPS, h=bl[2])
+    torch.cuda.synchronize()
+    assert torch.equal(bl[2], ref)
+
+
+@pytest.mark.parametrize("target", ["partial", "o"])
+def test_attnres_merge_output_may_alias_its_inputs(target):
+    n, L, T, d = 3, 2, 200, 512
+    V, W = ki.attnres_inputs(n + 1, T, d, L, 93370)
+    bl = blocks_dev(V)
+    o, lse = kda.attnres_inter(bl[:n], dev_io(W, "bf16"), EPS)
+    wd = dev_io(W[1], "bf16")
+    ref = kda.attnres_merge(bl[n], wd, o[1], lse[1], EPS).clone()
+    out = bl[n] if target == "partial" else o[1]
+    kda.attnres_merge(bl[n], wd, o[1], lse[1], EPS, h=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

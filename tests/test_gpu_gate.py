@@ -126,3 +126,20 @@ def test_fused_equals_prologue_then_fwd_bitwise(d):
     torch.cuda.synchronize()
     print(f"fused vs prologue+fwd d={d}: o equal {torch.equal(o1, o2)}, state equal {torch.equal(S1, S2)}")
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_gate_largest_rank_and_heads():
+    """r = 128 (four rank blocks), H = 64 heads (four beta tiles), d = 64."""
+    Ntok, Dm, H, d, r = 200, 256, 64, 64, 128
+    w_down, w_beta, w_up, b = ki.gate_weights(Dm, H, d, r, 93250)
+    x = ki.gate_hidden(Ntok, Dm, 93250)
+    z_g, beta_g, g_g = kda.gate(*upload_gate(x, w_down, w_beta, w_up, b), want_g=True)
+    torch.cuda.synchronize()
+    z_ref, beta_ref, _ = oracle.gate(x, w_down, w_beta, w_up, b, H, d)
+    z_st = ki.bf16_round(z_ref.astype(np.float32)).astype(np.float64)
+    same = np.all(host(z_g) == z_st, axis=1)
+    e_g = rel_inf(host(g_g)[same], oracle.gate_g(z_st, w_up, b, H, d)[same])
+    print(f"gate r=128 H=64: z err {floored_rel(host(z_g), z_ref):.2e}, beta err {rel_inf(host(beta_g), beta_ref):.2e}, "
+          f"g err {e_g:.2e} ({same.mean():.3f} identical z)")
+    assert floored_rel(host(z_g), z_ref) <= 4e-3 and rel_inf(host(beta_g), beta_ref) <= 1e-5
+    assert same.mean() >= 0.95 and e_g <= 1e-5
