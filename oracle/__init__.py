@@ -14,6 +14,10 @@ Contents
   attnres, attnres_logits, attnres_lse, rms_norm
                   Block AttnRes read-out: softmax over the blocks of w . norm(V_n), then the
                   weighted sum of the blocks V_n (numpy fp64).
+  segment_map, state_combine
+                  the affine map S_out = A S_in + B of a segment of one chain, and one hop
+                  of the prefix over segments (KCP context parallelism; numpy fp64 + the
+                  C recurrence).
 
 Sources (the pages this follows)
   * Course page "线性注意力与 KDA" (ai.air7.fun, Day 19), section 3: the decay
@@ -30,6 +34,8 @@ Sources (the pages this follows)
     down-up projection of the input; beta is a single scalar.  AttnRes section:
     softmax weights over the earlier blocks' outputs, summing to one; two-phase
     inference with an online-softmax merge.
+  * Blog post-114, chapter 3: chunks are processed in parallel inside and merged
+    serially into the state; K3's KCP extends that across devices (the segment map).
   * Blog post-114, chapter 6: the block AttnRes listing (stack the block outputs,
     normalise them as keys, score them with the layer's projection weight, softmax
     over the blocks, weighted sum).
@@ -326,3 +332,34 @@ def attnres_lse(V: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
     lg = attnres_logits(V, w, eps)
     m = lg.max(axis=0)
     return m + np.log(np.exp(lg - m[None, :]).sum(axis=0))
+
+
+# --------------------------------------------------------------------------- segment maps (KCP)
+def segment_map(k, v, g, beta):
+    """The affine map a segment of one chain applies to the state, fp64: S_out = A S_in + B.
+
+    Blog post-114, chapter 3: the chunked form computes each block's contribution in parallel
+    and merges it into the running state serially, and K3's KCP carries the same idea across
+    devices; a device's segment is then one large block whose contribution is this map.  Per
+    token the recurrence is S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+    (decay, then the delta write of the course page's section 3), so
+        A = prod over t, latest on the left, of (I - beta_t k_t k_t^T) Diag(alpha_t),
+        B = the state the recurrence reaches from S_0 = 0.
+    k, g [L, dk]; v [L, dv]; beta [L] (stored values).  Returns (A [dk, dk], B [dk, dv]).
+    A is the product written out token by token (numpy); B comes from the C recurrence.
+    """
+    k, g = np.asarray(k, np.float64), np.asarray(g, np.float64)
+    beta = np.asarray(beta, np.float64)
+    L, dk = k.shape
+    A = np.eye(dk)
+    for t in range(L):
+        A = np.exp(g[t])[:, None] * A                        # Diag(alpha_t) A
+        A = A - beta[t] * np.outer(k[t], k[t] @ A)           # (I - beta k k^T) ...
+    _, B = chain(np.zeros((L, dk), np.float32), k, v, g, beta, 1.0, None)
+    return A, B
+
+
+def state_combine(A, S, B):
+    """One hop of the prefix over segments: the state leaving a segment whose map is (A, B)
+    when S enters it, A S + B (fp64)."""
+    return np.asarray(A, np.float64) @ np.asarray(S, np.float64) + np.asarray(B, np.float64)
