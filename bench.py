@@ -10,10 +10,15 @@ The same run also measures
   * the prefill batch with one decay per token and head, and with none (kda_fwd_scalar_gate);
   * the long-context prefill (B = 1, H = 32, T = 131072) and the varlen layer (prologue on q
     and k, then the prefill of the packed 64-sequence batch): ms and tokens/s;
+  * the long-context prefill split into 8 segments of 16384 tokens (segment maps, the hop
+    between segments, the scan from the incoming states): one segment's kernels, and all
+    eight run on this GPU;
+  * the low-rank gate prologue and the fused prefill, and Block AttnRes (one-shot and
+    two-phase);
   * the fp64 CPU oracle on a bounded sample of the prefill workload (cpu_baseline).
 Per-kernel times come from HIP events recorded on the stream the kernels run on.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,scalar,gate,attnres,long,varlen,cpu,copy]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,decode,prep,scalar,gate,attnres,long,kcp,varlen,cpu,copy]
 Prints one JSON line.  `--only copy` runs a plain 256 MiB device copy (a kernel of known size
 used to calibrate the FETCH_SIZE / WRITE_SIZE counters of profiler runs).
 The roofline "traffic" figure comes from profiles/traffic.json (counter runs of this same
@@ -232,6 +237,84 @@ def bench_long(torch, kda, dev, reps=5):
             "ms": ms, "ms_chunk_local": ms_local, "ms_state_scan": ms_scan, "tokens_per_s": B * T / (ms / 1e3),
             "algorithmic_GBs": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * th / ms / 1e6,
             "hbm_frac": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * th / ms / 1e6 / HBM_PEAK_GBS}
+
+
+def bench_kcp(torch, kda, dev, reps=5):
+    """Segment maps (context parallelism): the long-context workload (B=1, H=32, T=131072, d=128,
+    bf16, S_0 given) split into 8 segments of 16384 tokens.  (a) One segment, the share of one
+    device in an 8-way split: chunk records, the segment map (A, B), one hop (kda_state_combine
+    over the 32 heads) and the scan from the incoming state.  (b) All 8 segments on this GPU:
+    records and maps of every segment in one launch each, the 7 serial hops, one scan."""
+    P, Ts, H, d = 8, 16384, 32, 128
+    T = P * Ts
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93007)
+    rnd = lambda *shape: torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+    q, k = _unit_bf16(rnd(1, T, H, d)), _unit_bf16(rnd(1, T, H, d))
+    v = rnd(1, T, H, d).to(torch.bfloat16)
+    beta = torch.sigmoid(rnd(1, T, H))
+    g = -torch.nn.functional.softplus(rnd(1, T, H, d) + 2)
+    S0 = rnd(1, H, d, d) * 0.02
+    L = kda.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()
+    B16 = kda.KDA_BF16
+
+    # (a) one device's share: the first segment's tokens as a dense batch of one sequence
+    qs, ks, vs, gs, bs = (x[:, :Ts].contiguous() for x in (q, k, v, g, beta))
+    nws1 = kda.fwd_workspace_bytes(B16, 1, Ts, H, d, d, 1, False)
+    ws1 = torch.empty(nws1, dtype=torch.uint8, device=dev)
+    A1 = torch.empty((1, H, d, d), dtype=torch.float32, device=dev)
+    B1 = torch.empty_like(A1)
+    S_next = torch.empty_like(A1)
+    S_end = torch.empty_like(A1)
+    o1 = torch.empty((1, Ts, H, d), dtype=torch.bfloat16, device=dev)
+
+    def local1():
+        assert L.kda_fwd_chunk_local(B16, 1, Ts, H, d, d, None, 1, p(qs), p(ks), p(vs), p(gs), p(bs), p(ws1),
+                                     nws1, st) == 0
+
+    def map1():
+        assert L.kda_fwd_segment_map(B16, 1, Ts, H, d, d, None, 1, p(A1), p(B1), p(ws1), nws1, st) == 0
+
+    def hop1():
+        assert L.kda_state_combine(H, d, d, p(A1), p(S0), p(B1), p(S_next), st) == 0
+
+    def scan1():
+        assert L.kda_fwd_state_scan(B16, 1, Ts, H, d, d, None, 1, 1.0, p(S0), p(S_end), p(o1), p(ws1), nws1,
+                                    st) == 0
+
+    # (b) all segments on this GPU
+    cu = torch.arange(0, T + 1, Ts, dtype=torch.int32, device=dev)
+    nws = kda.fwd_workspace_bytes(B16, 1, T, H, d, d, P, True)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    A = torch.empty((P, H, d, d), dtype=torch.float32, device=dev)
+    Bm = torch.empty_like(A)
+    S_in = torch.empty_like(A)
+    S_out = torch.empty_like(A)
+    o = torch.empty((1, T, H, d), dtype=torch.bfloat16, device=dev)
+    seg = H * d * d * 4  # bytes of one segment's maps or states
+
+    def whole():
+        assert L.kda_fwd_chunk_local(B16, 1, T, H, d, d, p(cu), P, p(q), p(k), p(v), p(g), p(beta), p(ws), nws,
+                                     st) == 0
+        assert L.kda_fwd_segment_map(B16, 1, T, H, d, d, p(cu), P, p(A), p(Bm), p(ws), nws, st) == 0
+        S_in[0].copy_(S0[0])
+        for j in range(P - 1):
+            assert L.kda_state_combine(H, d, d, p(A) + j * seg, p(S_in) + j * seg, p(Bm) + j * seg,
+                                       p(S_in) + (j + 1) * seg, st) == 0
+        assert L.kda_fwd_state_scan(B16, 1, T, H, d, d, p(cu), P, 1.0, p(S_in), p(S_out), p(o), p(ws), nws,
+                                    st) == 0
+
+    local1(); map1(); hop1(); scan1(); whole()
+    torch.cuda.synchronize()
+    ms_l, ms_m = time_events(local1, reps, torch), time_events(map1, reps, torch)
+    ms_h, ms_s = time_events(hop1, 20, torch), time_events(scan1, reps, torch)
+    ms_w = time_events(whole, reps, torch)
+    return {"workload": "KDA prefill B=1 H=32 T=131072 d=128 bf16, S_0 given, in 8 segments of 16384",
+            "segment_ms": {"chunk_local": ms_l, "segment_map": ms_m, "hop": ms_h, "state_scan": ms_s},
+            "segment_map_overhead": (ms_m + ms_h) / (ms_l + ms_s),
+            "all_segments_one_gpu_ms": ms_w, "all_segments_tokens_per_s": T / (ms_w / 1e3)}
 
 
 def bench_scalar_gate(torch, kda, dev, reps=20):
@@ -480,8 +563,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,attnres,long,varlen,cpu",
-                    help="comma list of prefill, decode, prep, scalar, gate, attnres, long, varlen, cpu, copy")
+    ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,attnres,long,kcp,varlen,cpu",
+                    help="comma list of prefill, decode, prep, scalar, gate, attnres, long, kcp, varlen, cpu, "
+                         "copy")
     args = ap.parse_args()
     only = set(x.strip() for x in args.only.split(",") if x.strip())
     if args.gpus != 1:
@@ -507,6 +591,8 @@ def main():
             out["attnres"] = bench_attnres(torch, kda, dev)
         if "long" in only:
             out["long_context"] = bench_long(torch, kda, dev)
+        if "kcp" in only:
+            out["segment_maps"] = bench_kcp(torch, kda, dev)
         if "varlen" in only:
             out["varlen_layer"] = bench_varlen_layer(torch, kda, dev)
         if "copy" in only:
@@ -577,6 +663,9 @@ def main():
     if "long" in only:
         log("long context ...")
         out["long_context"] = bench_long(torch, kda, dev)
+    if "kcp" in only:
+        log("segment maps ...")
+        out["segment_maps"] = bench_kcp(torch, kda, dev)
     if "varlen" in only:
         log("varlen layer ...")
         out["varlen_layer"] = bench_varlen_layer(torch, kda, dev)

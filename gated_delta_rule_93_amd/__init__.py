@@ -13,6 +13,9 @@ library is missing, importing works but the first call raises.
     h          = attnres(blocks, w, eps)                     # Block AttnRes read-out
     o, lse     = attnres_inter(blocks, W, eps)               # phase 1 for L layers
     h          = attnres_merge(partial, w, o_l, lse_l, eps)  # phase 2 for one layer
+    A, B       = fwd_segment_map(fwd_chunk_local(...), ...)  # S_out = A S_in + B per chain
+    S_next     = state_combine(A, S_in, B)                 # one hop between segments
+    o, S, ...  = fwd_segmented(q, k, v, g, beta, seg_bounds)  # one sequence in P segments
 
 Layouts: q, k, g [B, T, H, dk]; v, o [B, T, H, dv]; beta [B, T, H]; states [N, H, dk, dv]
 fp32 with element (i, j) mapping key channel i to value channel j (o = S^T q).  q, k, v
@@ -76,6 +79,10 @@ def lib():
         L.kda_attnres_inter.restype = I
         L.kda_attnres_merge.argtypes = [I, I, I, P, P, F, P, P, P, P]
         L.kda_attnres_merge.restype = I
+        L.kda_fwd_segment_map.argtypes = [I, I, I, I, I, I, P, I, P, P, P, S, P]
+        L.kda_fwd_segment_map.restype = I
+        L.kda_state_combine.argtypes = [I, I, I, P, P, P, P, P]
+        L.kda_state_combine.restype = I
         _lib = L
     return _lib
 
@@ -238,6 +245,110 @@ def _fwd(kind, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_
               _ptr(initial_state), _ptr(final_state), _ptr(o),
               _ptr(workspace), workspace.numel(), _stream(stream)))
     return o, final_state
+
+
+def fwd_chunk_local(q, k, v, g, beta, cu_seqlens=None, workspace=None, stream=None):
+    """First phase of kda_fwd (kda_fwd_chunk_local): the chunk records, into `workspace` (returned)."""
+    torch = _torch()
+    io = _io_dtype(q)
+    B, T, H, dk = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (B, T, H, dk))
+    _need(v, "v", q.dtype, (B, T, H, dk))
+    _need(g, "g", torch.float32, (B, T, H, dk))
+    _need(beta, "beta", torch.float32, (B, T, H))
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32)
+    need = fwd_workspace_bytes(io, B, T, H, dk, dk, N, cu_seqlens is not None)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(lib().kda_fwd_chunk_local(io, B, T, H, dk, dk, _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(g), _ptr(beta), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return workspace
+
+
+def fwd_state_scan(workspace, io: int, B: int, T: int, H: int, dk: int, cu_seqlens=None, scale: float = 1.0,
+                   initial_state=None, o=None, final_state=None, stream=None):
+    """Second phase of kda_fwd (kda_fwd_state_scan) over the records in `workspace`.
+    Returns (o [B, T, H, dk], final_state [N, H, dk, dk])."""
+    torch = _torch()
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dt = torch.bfloat16 if io == KDA_BF16 else torch.float32
+    dev = workspace.device
+    o = torch.empty((B, T, H, dk), dtype=dt, device=dev) if o is None else _need(o, "o", dt, (B, T, H, dk))
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dk), dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, (N, H, dk, dk))
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, dk, dk))
+    _check(lib().kda_fwd_state_scan(io, B, T, H, dk, dk, _ptr(cu_seqlens), N, float(scale), _ptr(initial_state),
+                                    _ptr(final_state), _ptr(o), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
+    return o, final_state
+
+
+def fwd_segment_map(workspace, io: int, B: int, T: int, H: int, dk: int, cu_seqlens=None,
+                    transition=None, offset=None, stream=None):
+    """Affine map S_out = A S_in + B of every chain (kda_fwd_segment_map), from the records that
+    fwd_chunk_local left in `workspace`.  Returns (A [N, H, dk, dk], B [N, H, dk, dk])."""
+    torch = _torch()
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = workspace.device
+    if transition is None:
+        transition = torch.empty((N, H, dk, dk), dtype=torch.float32, device=dev)
+    if offset is None:
+        offset = torch.empty((N, H, dk, dk), dtype=torch.float32, device=dev)
+    _need(transition, "transition", torch.float32, (N, H, dk, dk))
+    _need(offset, "offset", torch.float32, (N, H, dk, dk))
+    _check(lib().kda_fwd_segment_map(io, B, T, H, dk, dk, _ptr(cu_seqlens), N, _ptr(transition), _ptr(offset),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+    return transition, offset
+
+
+def state_combine(transition, state_in, offset, out=None, stream=None):
+    """out = transition @ state_in + offset over the leading dimensions (kda_state_combine, fp32)."""
+    torch = _torch()
+    d = transition.shape[-1]
+    lead = tuple(transition.shape[:-2])
+    _need(transition, "transition", torch.float32)
+    _need(state_in, "state_in", torch.float32, transition.shape)
+    _need(offset, "offset", torch.float32, transition.shape)
+    out = torch.empty_like(state_in) if out is None else out
+    if out.data_ptr() != offset.data_ptr():
+        _need(out, "out", torch.float32, transition.shape)
+    count = 1
+    for x in lead:
+        count *= int(x)
+    _check(lib().kda_state_combine(count, d, d, _ptr(transition), _ptr(state_in), _ptr(offset), _ptr(out),
+                                   _stream(stream)))
+    return out
+
+
+def fwd_segmented(q, k, v, g, beta, seg_bounds, scale: float = 1.0, initial_state=None, stream=None):
+    """One sequence (B = 1) split at `seg_bounds` (int32 device tensor [P + 1], 0 .. T) into P
+    segments and run as a context-parallel job would run it, here on one device: the chunk
+    records and the affine map of every segment (all segments at once), the P - 1 hops of the
+    prefix over segments (kda_state_combine, serial), then the state scan of every segment from
+    its incoming state.  Returns (o [1, T, H, dk], final_state [1, H, dk, dk], transition,
+    offset, incoming states [P, H, dk, dk])."""
+    torch = _torch()
+    io = _io_dtype(q)
+    B, T, H, dk = q.shape
+    if B != 1:
+        raise ValueError("fwd_segmented takes one sequence (B = 1)")
+    P = seg_bounds.numel() - 1
+    ws = fwd_chunk_local(q, k, v, g, beta, seg_bounds, stream=stream)
+    A, Bm = fwd_segment_map(ws, io, 1, T, H, dk, seg_bounds, stream=stream)
+    S_in = torch.empty((P, H, dk, dk), dtype=torch.float32, device=q.device)
+    if initial_state is None:
+        S_in[0].zero_()
+    else:
+        S_in[0].copy_(_need(initial_state, "initial_state", torch.float32, (1, H, dk, dk))[0])
+    for j in range(P - 1):
+        state_combine(A[j], S_in[j], Bm[j], out=S_in[j + 1], stream=stream)
+    o, S_out = fwd_state_scan(ws, io, 1, T, H, dk, seg_bounds, scale, S_in, stream=stream)
+    return o, S_out[P - 1:P], A, Bm, S_in
 
 
 def decode_step(q, k, v, g, beta, state, scale: float = 1.0, o=None, stream=None):

@@ -9,6 +9,11 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 bool supported_d(int d) { return d == 64 || d == 128; }
 bool valid_dtype(kda_dtype_t io) { return io == KDA_F32 || io == KDA_BF16; }
+// true when the byte ranges [a, a + na) and [b, b + nb) share a byte
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
 
 }  // namespace
 
@@ -86,6 +91,7 @@ kda::FwdArgs fwd_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, con
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.scalar_gate = false; a.scale = scale;
     a.s0 = s0; a.sN = sN; a.o = o; a.ws = workspace;
     a.gate_z = nullptr; a.gate_w_up = nullptr; a.gate_b = nullptr; a.gate_r = 0;
+    a.map_A = nullptr;
     return a;
 }
 
@@ -258,6 +264,39 @@ kda_status_t kda_fwd_state_scan(kda_dtype_t io, int B, int T, int H, int d_k, in
     const kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, nullptr, nullptr, nullptr, nullptr,
                                     nullptr, scale, initial_state, final_state, o, workspace);
     return kda::launch_fwd_scan(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_fwd_segment_map(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,
+                                 int N, float *transition, float *offset, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+    kda_status_t st = check_fwd(0, io, B, T, H, d_k, d_v, cu_seqlens, N, nullptr, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes);
+    if (st != KDA_OK || (long)N * H == 0) return st;
+    if (!transition || !offset || !aligned16(transition) || !aligned16(offset)) return KDA_ERR_INVALID_ARGUMENT;
+    const size_t bytes = (size_t)N * H * d_k * d_v * sizeof(float);
+    if (overlaps(transition, bytes, offset, bytes)) return KDA_ERR_INVALID_ARGUMENT;
+    kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, nullptr, nullptr, nullptr, nullptr, nullptr,
+                              1.f, nullptr, offset, nullptr, workspace);
+    a.map_A = transition;
+    return kda::launch_fwd_segment_map(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_state_combine(int count, int d_k, int d_v, const float *transition, const float *state_in,
+                               const float *offset, float *state_out, hipStream_t stream) {
+    if (count < 0 || d_k <= 0 || d_v <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (d_k != d_v || !supported_d(d_k)) return KDA_ERR_UNSUPPORTED;
+    if (count > (1 << 26)) return KDA_ERR_UNSUPPORTED;  // grid size
+    if (count == 0) return KDA_OK;
+    if (!transition || !state_in || !offset || !state_out) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(transition) || !aligned16(state_in) || !aligned16(offset) || !aligned16(state_out))
+        return KDA_ERR_INVALID_ARGUMENT;
+    const size_t bytes = (size_t)count * d_k * d_v * sizeof(float);
+    if (overlaps(state_out, bytes, transition, bytes) || overlaps(state_out, bytes, state_in, bytes))
+        return KDA_ERR_INVALID_ARGUMENT;
+    if (offset != state_out && overlaps(state_out, bytes, offset, bytes)) return KDA_ERR_INVALID_ARGUMENT;
+    return kda::launch_state_combine(count, d_k, transition, state_in, offset, state_out, stream) == hipSuccess
+               ? KDA_OK
+               : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_decode_step(kda_dtype_t io, int N, int H, int d_k, int d_v, const void *q, const void *k,

@@ -880,11 +880,23 @@ template <bool BF16, int D> struct ScanStage {
 template <bool BF16, int D, int NCT, int NS>
 constexpr int scan_threads() { return 64 * (NS * NCT + ScanStage<BF16, D>::kNP); }
 
-template <bool BF16, int D, int NCT, int NS>
+// Wave-loads of the staged block that the segment map reads: W, Kh^T and e^gamma (Qh and Aqk
+// only serve the read-out).
+template <bool BF16, int D> constexpr bool map_needs_load(int i) {
+    using L = WsLayout<BF16, D>;
+    return i < (int)(L::offQ / 1024) || (i >= (int)(L::offK / 1024) && i < (int)(L::offA / 1024)) ||
+           i >= (int)(L::offE / 1024);
+}
+
+// MAP = true: the segment map instead of the read-out.  Every chain gets twice the workgroups:
+// the first GPC run the chunks from S = 0 with the chunks' U (the offset B, into sN), the other
+// GPC from S = I with U taken as zero (the linear part A, into sA); no output rows, no Qh S.
+template <bool BF16, int D, int NCT, int NS, bool MAP = false>
 __global__ void __launch_bounds__((scan_threads<BF16, D, NCT, NS>()))
 chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
                   const float *__restrict__ s0, float *__restrict__ sN,
-                  typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws) {
+                  typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws,
+                  float *__restrict__ sA) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     using P = Prec<BF16>;
     using L = WsLayout<BF16, D>;
@@ -905,13 +917,16 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     __shared__ __attribute__((aligned(16))) char stage1[kProd ? St::bytes : 16];
     __shared__ f32x4 xws[NCT][NS][4][64];  // [tile][from part][token tile][lane]: W S partials
     // Qh S partials of the tiles a part does not own: [tile][from part][slot][lane]
-    __shared__ f32x4 xqs[NCT][NS][4 - NOT][64];
-    __shared__ __attribute__((aligned(16))) TIO obuf[kProd ? kChunk : 1][kProd ? OC : 1];  // output rows
+    __shared__ f32x4 xqs[MAP ? 1 : NCT][MAP ? 1 : NS][MAP ? 1 : 4 - NOT][64];
+    __shared__ __attribute__((aligned(16))) TIO obuf[kProd && !MAP ? kChunk : 1][kProd && !MAP ? OC : 1];  // output rows
 
     // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
+    constexpr int NG = MAP ? 2 * GPC : GPC;  // workgroups per chain
     const int b = blockIdx.x, xcd = b & 7, sl = b >> 3;
-    const int jg = sl % GPC, chain = (sl / GPC) * 8 + xcd;
+    const int jgm = sl % NG, chain = (sl / NG) * 8 + xcd;
     if (chain >= nchains) return;  // uniform over the workgroup
+    const bool amap = MAP && jgm >= GPC;  // this workgroup forms columns of A
+    const int jg = amap ? jgm - GPC : jgm;
     const int n = chain / H, h = chain % H;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
     const bool producer = kProd && wave >= NW;
@@ -958,7 +973,8 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             char *dst = decltype(bufc)::value ? stage1 : stage0;
             const char *src = record(c);
 #pragma unroll
-            for (int i = 0; i < St::kLoads; ++i) copy_one(src, dst, i);
+            for (int i = 0; i < St::kLoads; ++i)
+                if (!MAP || map_needs_load<BF16, D>(i)) copy_one(src, dst, i);
         };
         const int pw = wave - NW;  // this producer copies the chunks c with c % 2 == pw
         if (pw < nck) {
@@ -1010,13 +1026,18 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int i = j * NW + wave;
-            if (i < St::kLoads) copy_one(record(c), stage0, i);
+            if (i < St::kLoads && (!MAP || map_needs_load<BF16, D>(i))) copy_one(record(c), stage0, i);
         }
     };
     // U tiles alternate between two register sets (even chunks in uA, odd in uB), so a
     // prefetched tile is never copied between registers before it has arrived
     f32x4 uA[4], uB[4];
     auto prefetch_u = [&](long c, f32x4 (&u)[4]) __attribute__((always_inline)) {
+        if (amap) {  // the linear part: U is zero
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) u[tt] = zero4();
+            return;
+        }
         const f32x4 *pu = reinterpret_cast<const f32x4 *>(record(c) + L::offU) + jt * 4 * 64 + lane;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) u[tt] = pu[tt * 64];
@@ -1028,7 +1049,8 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     for (int r = 0; r < RTH; ++r)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            S[r][e] = s0 ? s0[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] : 0.f;
+            S[r][e] = MAP ? (amap && 16 * (part * RTH + r) + 4 * grp + e == col ? 1.f : 0.f)
+                          : s0 ? s0[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] : 0.f;
 
     if (nck > 0) {
         if (!kProd) stage_all(0);
@@ -1054,7 +1076,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
                 for (int kk = 0; kk < KBH; ++kk) {
                     wf[tt][kk] = ldW(tt, kk);
-                    qf[tt][kk] = ldQ(tt, kk);
+                    if constexpr (!MAP) qf[tt][kk] = ldQ(tt, kk);
                 }
         }
         if (more) prefetch_u(c + 1, u_nx);
@@ -1072,13 +1094,14 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
             for (int tt = 0; tt < 4; ++tt) {
                 wsa[tt] = mfma(BF16 ? wf[tt][kk] : ldW(tt, kk), sop, wsa[tt]);
-                qsa[tt] = mfma(BF16 ? qf[tt][kk] : ldQ(tt, kk), sop, qsa[tt]);
+                if constexpr (!MAP) qsa[tt] = mfma(BF16 ? qf[tt][kk] : ldQ(tt, kk), sop, qsa[tt]);
             }
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             xws[ct][part][tt][lane] = wsa[tt];
-            if (!owns(part, tt)) xqs[ct][part][qslot(part, tt)][lane] = qsa[tt];
+            if constexpr (!MAP)
+                if (!owns(part, tt)) xqs[ct][part][qslot(part, tt)][lane] = qsa[tt];
         }
         // operands of the second part of the chunk, requested before the barrier
         // (with a producer the buffer is refilled right after the exchange barrier, so every
@@ -1094,11 +1117,13 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         }
         // Aqk fragments of the own output tiles: one k-block for tiles 0 and 1, two for 2 and 3
         Split af[NOT][2];
+        if constexpr (!MAP) {
 #pragma unroll
-        for (int i = 0; i < NOT; ++i) {
-            const int ot = own_tile(i);
-            af[i][0] = P::ld_split(sb + L::offA, L::nA, aidx(ot, 0), lane);
-            af[i][1] = P::ld_split(sb + L::offA, L::nA, aidx(ot, ot >= 2 ? 1 : 0), lane);
+            for (int i = 0; i < NOT; ++i) {
+                const int ot = own_tile(i);
+                af[i][0] = P::ld_split(sb + L::offA, L::nA, aidx(ot, 0), lane);
+                af[i][1] = P::ld_split(sb + L::offA, L::nA, aidx(ot, ot >= 2 ? 1 : 0), lane);
+            }
         }
         f32x4 e_cur[RTH];
 #pragma unroll
@@ -1106,7 +1131,8 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (part * RTH + r) + 4 * grp));
         // rows of the previous chunk (left in obuf before the top barrier; refilled after the
         // exchange barrier)
-        if (kProd && c > 0) store_rows(c - 1);
+        if constexpr (!MAP)
+            if (kProd && c > 0) store_rows(c - 1);
         // exchange barrier: only LDS traffic must be complete (lgkmcnt); copies into the other
         // stage buffer stay in flight (a fence here would wait for them too)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1130,7 +1156,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         // the state update; the products that need only the first k-block of Ud come first
         f32x4 oo[NOT], Sn[RTH];
 #pragma unroll
-        for (int i = 0; i < NOT; ++i) {
+        for (int i = 0; i < (MAP ? 0 : NOT); ++i) {
             const int ot = own_tile(i);
             const f32x4 mine = ot == 0 ? qsa[0] : ot == 1 ? qsa[1] : ot == 2 ? qsa[2] : qsa[3];
             oo[i] = part == 0 ? mine : xqs[ct][0][qslot(0, ot)][lane];
@@ -1140,31 +1166,33 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
         for (int r = 0; r < RTH; ++r) Sn[r] = S[r] * e_cur[r];
 #pragma unroll
-        for (int i = 0; i < NOT; ++i) oo[i] = mfma(af[i][0], Uop[0], oo[i]);
+        for (int i = 0; i < (MAP ? 0 : NOT); ++i) oo[i] = mfma(af[i][0], Uop[0], oo[i]);
 #pragma unroll
         for (int r = 0; r < RTH; ++r) Sn[r] = mfma(kEarlyK ? kf[r][0] : ldK(r, 0), Uop[0], Sn[r]);
 #pragma unroll
-        for (int i = 0; i < NOT; ++i)
+        for (int i = 0; i < (MAP ? 0 : NOT); ++i)
             if (own_tile(i) >= 2) oo[i] = mfma(af[i][1], Uop[1], oo[i]);
 #pragma unroll
         for (int r = 0; r < RTH; ++r) S[r] = mfma(kEarlyK ? kf[r][1] : ldK(r, 1), Uop[1], Sn[r]);
         if (kProd) {
             // rows of this chunk (the previous ones were read before the exchange barrier)
 #pragma unroll
-            for (int i = 0; i < NOT; ++i)
+            for (int i = 0; i < (MAP ? 0 : NOT); ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     IO<TIO>::store(&obuf[16 * own_tile(i) + 4 * grp + e][0], ct * 16 + r16, scale * oo[i][e]);
         } else {
-            const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
-            TIO *ob = o + ((s_tok + c * kChunk) * H + h) * (long)D + col;
+            if constexpr (!MAP) {
+                const int Cc = (int)min((long)kChunk, L_n - c * kChunk);
+                TIO *ob = o + ((s_tok + c * kChunk) * H + h) * (long)D + col;
 #pragma unroll
-            for (int i = 0; i < NOT; ++i)
+                for (int i = 0; i < NOT; ++i)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = 16 * own_tile(i) + 4 * grp + e;
-                    if (t < Cc) IO<TIO>::store(ob, (long)t * HD, scale * oo[i][e]);
-                }
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 16 * own_tile(i) + 4 * grp + e;
+                        if (t < Cc) IO<TIO>::store(ob, (long)t * HD, scale * oo[i][e]);
+                    }
+            }
             if (more) {
                 __syncthreads();  // every wave is done with the single buffer
                 stage_all(c + 1);
@@ -1176,15 +1204,17 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         if (c + 1 < nck) chunk_step(c + 1, std::integral_constant<int, kProd ? 1 : 0>{}, uB, uA);
     }
     if (kProd) {
-        __syncthreads();  // the last chunk's rows are in obuf
-        if (nck > 0) store_rows(nck - 1);
+        __syncthreads();  // the last chunk's rows are in obuf (and pairs with the producers' last barrier)
+        if constexpr (!MAP)
+            if (nck > 0) store_rows(nck - 1);
     }
-    if (sN) {
+    float *const sout = amap ? sA : sN;
+    if (sout) {
 #pragma unroll
         for (int r = 0; r < RTH; ++r)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                sN[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] = S[r][e];
+                sout[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] = S[r][e];
     }
 }
 
@@ -1211,13 +1241,14 @@ static hipError_t launch_local_t(const FwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <bool BF16, int D, int NCT, int NS>
+template <bool BF16, int D, int NCT, int NS, bool MAP>
 static hipError_t launch_scan_nct(const FwdArgs &a, hipStream_t st, int nchains) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
-    const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NCT);
-    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT, NS>), dim3((unsigned)blocks),
+    const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NCT) * (MAP ? 2 : 1);
+    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT, NS, MAP>), dim3((unsigned)blocks),
                        dim3(scan_threads<BF16, D, NCT, NS>()), 0, st,
-                       a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale, a.s0, a.sN, (TIO *)a.o, (const char *)a.ws);
+                       a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale, MAP ? nullptr : a.s0, a.sN, (TIO *)a.o,
+                       (const char *)a.ws, MAP ? a.map_A : nullptr);
     return hipGetLastError();
 }
 
@@ -1238,17 +1269,18 @@ static int device_cu_count() {
 
 // Column tiles per workgroup: two when that still gives every CU a workgroup (the tiles then
 // share one LDS copy of the chunk's operands), else one with the state split over more waves.
-template <bool BF16, int D>
+// The segment map (MAP) has twice the column tiles: those of B and those of A.
+template <bool BF16, int D, bool MAP = false>
 static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
     const int nchains = a.N * a.H;
     if (nchains <= 0) return hipSuccess;
     const int cus = device_cu_count();
-    const long tiles = (long)nchains * (D / 16);
-    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2, 2>(a, st, nchains);
+    const long tiles = (long)nchains * (D / 16) * (MAP ? 2 : 1);
+    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2, 2, MAP>(a, st, nchains);
     // too few tiles to give every CU a two-tile workgroup: one tile per workgroup, and at
     // d = 128 four waves per tile (a shorter serial chain per chunk)
-    if constexpr (D == 128) return launch_scan_nct<BF16, D, 1, 4>(a, st, nchains);
-    else return launch_scan_nct<BF16, D, 1, 2>(a, st, nchains);
+    if constexpr (D == 128) return launch_scan_nct<BF16, D, 1, 4, MAP>(a, st, nchains);
+    else return launch_scan_nct<BF16, D, 1, 2, MAP>(a, st, nchains);
 }
 
 template <bool BF16, int D>
@@ -1277,6 +1309,11 @@ hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {
 hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st) {
     if (a.bf16) return a.dk == 128 ? launch_scan_t<true, 128>(a, st) : launch_scan_t<true, 64>(a, st);
     return a.dk == 128 ? launch_scan_t<false, 128>(a, st) : launch_scan_t<false, 64>(a, st);
+}
+
+hipError_t launch_fwd_segment_map(const FwdArgs &a, hipStream_t st) {
+    if (a.bf16) return a.dk == 128 ? launch_scan_t<true, 128, true>(a, st) : launch_scan_t<true, 64, true>(a, st);
+    return a.dk == 128 ? launch_scan_t<false, 128, true>(a, st) : launch_scan_t<false, 64, true>(a, st);
 }
 
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st) {

@@ -45,6 +45,7 @@ struct FwdArgs {
     float *sN;
     void *o;
     void *ws;
+    float *map_A;               // segment map only: the linear part A [N, H, dk, dk] (sN receives B)
 };
 // Bytes of workspace for one (chunk, head) and the number of chunk slots.
 size_t fwd_bytes_per_chunk_head(bool bf16, int d);
@@ -52,6 +53,13 @@ long fwd_chunk_slots(int B, int T, int N, bool varlen);
 hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);          // both phases
 hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st);    // chunk-local phase
 hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st);     // state-scan phase
+// The affine map S_out = A S_in + B of every (sequence, head) chain, from the chunk-local records
+// (a.map_A receives A, a.sN receives B; s0 and o are not used).
+hipError_t launch_fwd_segment_map(const FwdArgs &a, hipStream_t st);
+
+// out[c] = A[c] S[c] + B[c] for c < count; A [count, d, d], S, B, out [count, d, d] fp32.
+hipError_t launch_state_combine(int count, int d, const float *A, const float *S, const float *B, float *out,
+                                hipStream_t st);
 
 struct GateArgs {
     int Ntok, Dm, H, d, r;

@@ -185,6 +185,46 @@ kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, 
                                   hipStream_t stream);
 
 /*
+ * Segment maps (context parallelism).  Blog post-114, chapter 3: the chunked form computes
+ * each block's contribution in parallel and merges the blocks into the state one after the
+ * other; K3's KCP carries this across devices.  Taking a device's segment of a sequence as one
+ * block, its contribution is the affine map the recurrence applies to the state entering it:
+ *     S_out = A S_in + B,   A = prod_t (I - beta_t k_t k_t^T) Diag(alpha_t)   (latest on the left)
+ *                           B = the state reached from S_in = 0.
+ * A caller that splits one sequence into P segments (packed as the sequences of a varlen batch,
+ * cu_seqlens = the segment boundaries) runs kda_fwd_chunk_local and kda_fwd_segment_map on all
+ * segments at once, chains the incoming states with kda_state_combine (S_in of segment j + 1 =
+ * A_j S_in(j) + B_j, P - 1 serial hops), and finishes with kda_fwd_state_scan from those
+ * incoming states, which writes every o and the final state.  The result equals kda_fwd over
+ * the whole sequence up to fp32 rounding of the states at the segment boundaries.
+ */
+
+/*
+ * kda_fwd_segment_map -- the affine map (A, B) of every (sequence, head) chain of a batch, from
+ * the records kda_fwd_chunk_local left in the workspace (same sizes, cu_seqlens and workspace).
+ *
+ *   transition  [N, H, d_k, d_k] fp32 out: A, element (i, j) maps key channel j of S_in to i
+ *   offset      [N, H, d_k, d_v] fp32 out: B, in the state layout
+ *   The two must not overlap.  A zero-length sequence gives A = I, B = 0.  Other arguments,
+ *   the workspace (kda_fwd_workspace_bytes) and the error behaviour are those of kda_fwd.
+ */
+kda_status_t kda_fwd_segment_map(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                 const int32_t *cu_seqlens, int N,
+                                 float *transition, float *offset,
+                                 void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_state_combine -- one hop between segments, for `count` maps at once (fp32, fixed order):
+ *     state_out[c] = transition[c] state_in[c] + offset[c]
+ *   transition  [count, d_k, d_k] fp32;  state_in, offset, state_out [count, d_k, d_v] fp32
+ *   Supported: d_k == d_v in {64, 128}.  state_out must not overlap transition or state_in; it
+ *   may be offset itself (exactly, not a shifted overlap).  count == 0 does nothing.
+ */
+kda_status_t kda_state_combine(int count, int d_k, int d_v, const float *transition,
+                               const float *state_in, const float *offset, float *state_out,
+                               hipStream_t stream);
+
+/*
  * Block AttnRes.  Blog post-114, chapter 6 (the block AttnRes listing): the outputs of the
  * earlier blocks of layers (and the current, partial block) are stacked, normalised into keys,
  * scored against the layer's projection weight w, and mixed with the softmax of the scores over

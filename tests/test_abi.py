@@ -241,3 +241,58 @@ def test_attnres_other_entries_reject_and_accept_empty():
     assert L.kda_attnres_merge(kda.KDA_BF16, 10, 640, FAKE, FAKE, 1e-6, FAKE, FAKE, FAKE, None) \
         == kda.KDA_ERR_UNSUPPORTED
     assert L.kda_attnres_merge(kda.KDA_BF16, 0, 512, None, None, 1e-6, None, None, None, None) == kda.KDA_OK
+
+
+def segmap_call(**over):
+    a = dict(io=kda.KDA_BF16, B=1, T=640, H=2, dk=128, dv=128, cu=FAKE, N=3, A=FAKE, Bm=FAKE + (1 << 24),
+             ws=FAKE, wsb=1 << 30)
+    a.update(over)
+    return kda.lib().kda_fwd_segment_map(a["io"], a["B"], a["T"], a["H"], a["dk"], a["dv"], a["cu"], a["N"],
+                                         a["A"], a["Bm"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(io=5), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(B=2), kda.KDA_ERR_INVALID_ARGUMENT),                     # varlen needs B = 1
+    (dict(A=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(Bm=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(A=FAKE + 4), kda.KDA_ERR_INVALID_ARGUMENT),              # misaligned
+    (dict(Bm=FAKE + 4096), kda.KDA_ERR_INVALID_ARGUMENT),          # overlaps A
+    (dict(dk=64, dv=128), kda.KDA_ERR_UNSUPPORTED),
+    (dict(ws=None), kda.KDA_ERR_WORKSPACE),
+    (dict(wsb=4096), kda.KDA_ERR_WORKSPACE),
+])
+def test_segment_map_rejects(over, code):
+    assert segmap_call(**over) == code
+
+
+def test_segment_map_empty_is_ok_without_launch():
+    assert segmap_call(H=0, A=None, Bm=None, ws=None, wsb=0) == kda.KDA_OK
+    assert segmap_call(N=0, T=0, A=None, Bm=None, ws=None, wsb=0) == kda.KDA_OK
+
+
+def combine_call(**over):
+    step = 128 * 128 * 4 * 4                                       # 4 maps of 128 x 128 fp32
+    a = dict(count=4, dk=128, dv=128, A=FAKE, S=FAKE + step, Bm=FAKE + 2 * step, out=FAKE + 3 * step)
+    a.update(over)
+    return kda.lib().kda_state_combine(a["count"], a["dk"], a["dv"], a["A"], a["S"], a["Bm"], a["out"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(count=-1), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(A=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), kda.KDA_ERR_INVALID_ARGUMENT),
+    (dict(S=FAKE + 8), kda.KDA_ERR_INVALID_ARGUMENT),              # misaligned
+    (dict(out=FAKE + 128 * 128 * 4 * 1), kda.KDA_ERR_INVALID_ARGUMENT),  # out overlaps A
+    (dict(out=FAKE + 128 * 128 * 4 * 5), kda.KDA_ERR_INVALID_ARGUMENT),  # out overlaps S
+    (dict(out=FAKE + 128 * 128 * 4 * 9), kda.KDA_ERR_INVALID_ARGUMENT),  # shifted overlap with offset
+    (dict(dk=96, dv=96), kda.KDA_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=64), kda.KDA_ERR_UNSUPPORTED),
+    (dict(count=1 << 27), kda.KDA_ERR_UNSUPPORTED),
+])
+def test_state_combine_rejects(over, code):
+    assert combine_call(**over) == code
+
+
+def test_state_combine_empty_is_ok_without_launch():
+    assert combine_call(count=0, A=None, S=None, Bm=None, out=None) == kda.KDA_OK
