@@ -8,26 +8,31 @@
 // The last identity lets one pass over the state produce both the update and the read-out:
 // the state is read once and written once (2 * d_k * d_v * 4 bytes per head and step).
 //
-// Mapping: one 256-thread workgroup per (n, h).  Thread t owns value columns
-// 4 * (t % (DV/4)) .. +3 and key rows i = t / (DV/4) + RG * m (m = 0 .. DK/RG - 1), where
-// RG = 256 / (DV/4) row groups.  A wave reads whole 16-byte column quads of consecutive rows,
-// so every state access is a fully coalesced dwordx4.  The column reductions p and r are a
-// per-thread partial sum over its rows followed by a fixed-order LDS reduction across the RG
-// row groups (deterministic).
+// Mapping: one workgroup of NT = DK * DV / 16 threads per (n, h) (1024 at d = 128), so every
+// thread holds four 16-byte pieces of the state.  Thread t owns value columns 4 * (t % (DV/4))
+// .. +3 and key rows i = t / (DV/4) + RG * m (m = 0 .. 3), where RG = NT / (DV/4) row groups.
+// A wave reads whole 16-byte column quads of consecutive rows, so every state access is a fully
+// coalesced dwordx4.  The column reductions p and r are a per-thread partial sum over its rows
+// followed by a fixed-order LDS reduction across the RG row groups (deterministic).  Measured on
+// the 256 x 32-head, d = 128 step: 16 rows per thread (256 threads) ran at 5.5 TB/s, 8 rows at
+// 5.5, 4 rows (1024 threads) at 5.8: each head's state then arrives with more requests in flight.
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+template <int DK, int DV> constexpr int decode_threads() { return DK * DV / 16; }
+
 template <typename TIO, int DK, int DV>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__((decode_threads<DK, DV>()))
 decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k, const TIO *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta, float scale,
                    float *__restrict__ state, TIO *__restrict__ o) {
+    constexpr int NT = decode_threads<DK, DV>();
     constexpr int TPR = DV / 4;          // threads per state row (one float4 each)
-    constexpr int RG = 256 / TPR;        // row groups
-    constexpr int RPT = DK / RG;         // rows per thread
-    static_assert(RG * TPR == 256 && RPT * RG == DK, "tile");
+    constexpr int RG = NT / TPR;         // row groups
+    constexpr int RPT = DK / RG;         // rows per thread (4)
+    static_assert(RG * TPR == NT && RPT * RG == DK && NT <= 1024 && NT >= kWave, "tile");
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
     __shared__ f32x4 s_p[RG][TPR], s_r[RG][TPR];
@@ -46,7 +51,7 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k, const T
         const int i = rg + RG * m;
         s[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (long)i * DV) + cq);
     }
-    for (int i = t; i < DK; i += 256) {
+    for (int i = t; i < DK; i += NT) {
         s_k[i] = IO<TIO>::load(k, head * DK + i);
         s_q[i] = IO<TIO>::load(q, head * DK + i);
         s_a[i] = __expf(g[head * DK + i]);
@@ -99,7 +104,7 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k, const T
 template <typename TIO, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     const long heads = (long)a.N * a.H;
-    hipLaunchKernelGGL((decode_step_kernel<TIO, DK, DV>), dim3((unsigned)heads), dim3(256), 0, st,
+    hipLaunchKernelGGL((decode_step_kernel<TIO, DK, DV>), dim3((unsigned)heads), dim3(decode_threads<DK, DV>()), 0, st,
                        (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.scale,
                        a.state, (TIO *)a.o);
     return hipGetLastError();

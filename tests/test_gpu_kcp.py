@@ -158,6 +158,12 @@ def test_segmented_single_segment_and_fp32():
     check_segmented(inp, [64, 1, 100, 135], "fp32 P=4")
 
 
+def test_segmented_zero_initial_state_and_empty_segments():
+    """No initial state (zero), and empty segments inside the split (their map is the identity)."""
+    inp = ki.make_dense(1, 700, 3, 128, 128, "bf16", 93222, s0_std=None, g_shift=-5.0)
+    check_segmented(inp, [0, 256, 0, 300, 144, 0], "bf16 S_0 = 0, empty segments")
+
+
 def test_segmented_long_context_p8_sampled():
     """The long-context workload (B=1, H=32, T=131072, S_0 given) split into 8 segments of 16384
     tokens, one per device of an 8-way split; sampled heads checked in full."""
