@@ -23,7 +23,7 @@ const char *kda_status_string(kda_status_t s) {
     switch (s) {
         case KDA_OK: return "KDA_OK: success";
         case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT: null pointer, bad size, misaligned buffer or bad dtype";
-        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid arguments that this build does not implement";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid arguments that the library does not implement";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
         case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     }
