@@ -306,16 +306,18 @@ def fwd_segment_map(workspace, io: int, B: int, T: int, H: int, dk: int, cu_seql
     return transition, offset
 
 
-def state_combine(transition, state_in, offset, out=None, stream=None):
-    """out = transition @ state_in + offset over the leading dimensions (kda_state_combine, fp32)."""
+def state_combine(transition, state_in, offset=None, out=None, stream=None):
+    """out = transition @ state_in + offset over the leading dimensions (kda_state_combine, fp32);
+    offset None is zero (then the call composes two transitions)."""
     torch = _torch()
     d = transition.shape[-1]
     lead = tuple(transition.shape[:-2])
     _need(transition, "transition", torch.float32)
     _need(state_in, "state_in", torch.float32, transition.shape)
-    _need(offset, "offset", torch.float32, transition.shape)
+    if offset is not None:
+        _need(offset, "offset", torch.float32, transition.shape)
     out = torch.empty_like(state_in) if out is None else out
-    if out.data_ptr() != offset.data_ptr():
+    if offset is None or out.data_ptr() != offset.data_ptr():
         _need(out, "out", torch.float32, transition.shape)
     count = 1
     for x in lead:

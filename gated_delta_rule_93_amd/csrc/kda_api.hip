@@ -287,13 +287,13 @@ kda_status_t kda_state_combine(int count, int d_k, int d_v, const float *transit
     if (d_k != d_v || !supported_d(d_k)) return KDA_ERR_UNSUPPORTED;
     if (count > (1 << 26)) return KDA_ERR_UNSUPPORTED;  // grid size
     if (count == 0) return KDA_OK;
-    if (!transition || !state_in || !offset || !state_out) return KDA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(transition) || !aligned16(state_in) || !aligned16(offset) || !aligned16(state_out))
+    if (!transition || !state_in || !state_out) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(transition) || !aligned16(state_in) || (offset && !aligned16(offset)) || !aligned16(state_out))
         return KDA_ERR_INVALID_ARGUMENT;
     const size_t bytes = (size_t)count * d_k * d_v * sizeof(float);
     if (overlaps(state_out, bytes, transition, bytes) || overlaps(state_out, bytes, state_in, bytes))
         return KDA_ERR_INVALID_ARGUMENT;
-    if (offset != state_out && overlaps(state_out, bytes, offset, bytes)) return KDA_ERR_INVALID_ARGUMENT;
+    if (offset && offset != state_out && overlaps(state_out, bytes, offset, bytes)) return KDA_ERR_INVALID_ARGUMENT;
     return kda::launch_state_combine(count, d_k, transition, state_in, offset, state_out, stream) == hipSuccess
                ? KDA_OK
                : KDA_ERR_LAUNCH;

@@ -9,7 +9,8 @@
 //
 // One 256-thread workgroup per 32 x 32 tile of one map's output.  Row block i0.. of A and column
 // block j0.. of S are staged in LDS; each thread forms 4 adjacent outputs with fused multiply-adds
-// over k in ascending order, then adds B (a fixed order: the result is reproducible).
+// over k in ascending order, then adds B (a fixed order: the result is reproducible).  With B
+// absent the same kernel composes two maps' linear parts (A2 A1), the step of a tree-shaped prefix.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -50,7 +51,8 @@ __global__ void __launch_bounds__(256) state_combine_kernel(const float *__restr
         acc.w = fmaf(a, s.w, acc.w);
     }
     const long off = c * D * D + (long)(i0 + ty) * D + j0 + 4 * tx;
-    const float4 b = *reinterpret_cast<const float4 *>(B + off);  // read before the write: out may be B
+    const float4 b = B ? *reinterpret_cast<const float4 *>(B + off)  // read before the write: out may be B
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
     *reinterpret_cast<float4 *>(out + off) = make_float4(acc.x + b.x, acc.y + b.y, acc.z + b.z, acc.w + b.w);
 }
 

@@ -217,6 +217,9 @@ kda_status_t kda_fwd_segment_map(kda_dtype_t io, int B, int T, int H, int d_k, i
  * kda_state_combine -- one hop between segments, for `count` maps at once (fp32, fixed order):
  *     state_out[c] = transition[c] state_in[c] + offset[c]
  *   transition  [count, d_k, d_k] fp32;  state_in, offset, state_out [count, d_k, d_v] fp32
+ *   offset may be NULL (taken as zero): with state_in = the transition of an earlier segment this
+ *   composes two maps, (A2, B2) after (A1, B1) = (A2 A1, A2 B1 + B2), the step of a prefix over
+ *   segments taken as a tree (log2 P rounds) instead of a chain.
  *   Supported: d_k == d_v in {64, 128}.  state_out must not overlap transition or state_in; it
  *   may be offset itself (exactly, not a shifted overlap).  count == 0 does nothing.
  */

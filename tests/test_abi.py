@@ -296,3 +296,9 @@ def test_state_combine_rejects(over, code):
 
 def test_state_combine_empty_is_ok_without_launch():
     assert combine_call(count=0, A=None, S=None, Bm=None, out=None) == kda.KDA_OK
+
+
+def test_state_combine_offset_checks():
+    # the offset may be NULL (taken as zero; exercised on the GPU), but when given it is checked
+    assert combine_call(Bm=FAKE + 4, count=0) == kda.KDA_OK       # count 0: nothing checked
+    assert combine_call(Bm=FAKE + 4) == kda.KDA_ERR_INVALID_ARGUMENT  # misaligned offset

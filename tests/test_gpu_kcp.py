@@ -114,6 +114,33 @@ def test_state_combine_parity(d):
     assert np.array_equal(host(Bd), out)
 
 
+def test_composed_maps_equal_the_map_of_the_concatenation():
+    """(A2, B2) after (A1, B1) = (A2 A1, A2 B1 + B2), formed with kda_state_combine (the offset
+    left out for A2 A1), against the map of the two segments as one: the step of a prefix over
+    segments taken as a tree."""
+    lengths = [200, 331]
+    inp = ki.make_varlen(lengths, 2, 128, 128, "bf16", 93223, s0_std=None, g_shift=-5.0)
+    cu = _bounds(lengths)
+    io = kda.KDA_BF16
+    q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    cu_d = torch.from_numpy(cu.astype(np.int32)).to(DEV)
+    ws = kda.fwd_chunk_local(q, k, v, dev_f32(inp.g), dev_f32(inp.beta), cu_d)
+    A, B = kda.fwd_segment_map(ws, io, 1, inp.T, inp.H, inp.dk, cu_d)
+    A12 = kda.state_combine(A[1], A[0])
+    B12 = kda.state_combine(A[1], B[0], B[1])
+    whole = torch.from_numpy(np.array([0, inp.T], np.int32)).to(DEV)
+    ws1 = kda.fwd_chunk_local(q, k, v, dev_f32(inp.g), dev_f32(inp.beta), whole)
+    Aw, Bw = kda.fwd_segment_map(ws1, io, 1, inp.T, inp.H, inp.dk, whole)
+    torch.cuda.synchronize()
+    worst_a = worst_b = 0.0
+    for h in range(inp.H):
+        A_ref, B_ref = oracle.segment_map(inp.k[0, :, h], inp.v[0, :, h], inp.g[0, :, h], inp.beta[0, :, h])
+        worst_a = max(worst_a, err_A(host(A12[h]), A_ref, "bf16"), err_A(host(Aw[0, h]), A_ref, "bf16"))
+        worst_b = max(worst_b, err(host(B12[h]), B_ref, "bf16"), err(host(Bw[0, h]), B_ref, "bf16"))
+    print(f"composed maps: A err {worst_a:.3e}, B err {worst_b:.3e}")
+    assert worst_a <= tol("bf16") and worst_b <= tol("bf16")
+
+
 def run_segmented(inp, seg_lengths):
     cu = _bounds(seg_lengths)
     assert cu[-1] == inp.T and inp.B == 1
