@@ -519,21 +519,30 @@ def cpu_baseline(inp, min_seconds=10.0):
         if wall >= min_seconds or passes >= 200:
             break
     tokens = inp.B * inp.T * passes
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "os_cpu_count": os.cpu_count(),
             "sample": f"{passes} whole passes over the prefill batch (all {inp.B * inp.H} (sequence, head) "
                       f"chains of {inp.T} tokens), fp64 token recurrence, {wall:.1f} s wall"}
 
 
-def bench_copy(torch, dev):
-    """256 MiB device-to-device copy: the reference kernel for counter calibration."""
-    x = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+def bench_copy(torch, dev, nbytes=1 << 28):
+    """Device-to-device copy of nbytes (the runtime's copy kernel).  256 MiB: the reference kernel
+    for counter calibration; 512 MiB (the decode state's size): the copy the decode step is set
+    against in the same run."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     x.fill_(1)
     y = torch.empty_like(x)
     for _ in range(3):
         y.copy_(x)
     torch.cuda.synchronize()
     ms = time_events(lambda: y.copy_(x), 5, torch)
-    return {"bytes_read": 1 << 28, "bytes_written": 1 << 28, "ms": ms, "GBs": 2 * (1 << 28) / ms / 1e6}
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "GBs": 2 * nbytes / ms / 1e6}
 
 
 def kernel_source_hash():
@@ -556,6 +565,20 @@ def measured_traffic(kernel):
         return None
     k = t.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def measured_mfma(kernel):
+    """rocprofv3 MfmaUtil (%) and issued bf16 MFMA flops per launch of `kernel` from
+    profiles/traffic.json, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("mfma", {}).get(kernel)
 
 
 def main():
@@ -634,6 +657,7 @@ def main():
                     "algorithmic_TFLOPs": flops / pf["ms_fwd_events"] / 1e9,
                     "mfma_frac_of_bf16_peak": flops / pf["ms_fwd_events"] / 1e9 / BF16_PEAK_TFLOPS,
                     "workspace_bytes_per_chunk_head": pf["ws_bytes_per_chunk_head"],
+                    "rocprof_mfma": {k: measured_mfma(k) for k in ("chunk_local_kernel", "chunk_scan_kernel")},
                     "untimed_settle_steps": pf["settle_steps"]},
     }
     if "decode" in only:
@@ -646,6 +670,9 @@ def main():
                                       "frac": dc["total_gbs"] / HBM_PEAK_GBS,
                                       "traffic": measured_traffic("decode_step_kernel"),
                                       "algorithmic_bytes_per_launch": dc["state_bytes"] + dc["io_bytes"]}}
+        cp = bench_copy(torch, dev, 1 << 29)
+        out["decode"]["copy_same_run"] = {"what": "runtime device copy of 512 MiB (read + write)",
+                                          "GBs": cp["GBs"], "decode_over_copy": dc["total_gbs"] / cp["GBs"]}
     if "prep" in only:
         log("prep ...")
         pr = bench_prep(args, torch, kda, dev)

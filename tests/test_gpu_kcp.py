@@ -132,13 +132,15 @@ def test_composed_maps_equal_the_map_of_the_concatenation():
     ws1 = kda.fwd_chunk_local(q, k, v, dev_f32(inp.g), dev_f32(inp.beta), whole)
     Aw, Bw = kda.fwd_segment_map(ws1, io, 1, inp.T, inp.H, inp.dk, whole)
     torch.cuda.synchronize()
-    worst_a = worst_b = 0.0
+    direct = composed = 0.0
     for h in range(inp.H):
         A_ref, B_ref = oracle.segment_map(inp.k[0, :, h], inp.v[0, :, h], inp.g[0, :, h], inp.beta[0, :, h])
-        worst_a = max(worst_a, err_A(host(A12[h]), A_ref, "bf16"), err_A(host(Aw[0, h]), A_ref, "bf16"))
-        worst_b = max(worst_b, err(host(B12[h]), B_ref, "bf16"), err(host(Bw[0, h]), B_ref, "bf16"))
-    print(f"composed maps: A err {worst_a:.3e}, B err {worst_b:.3e}")
-    assert worst_a <= tol("bf16") and worst_b <= tol("bf16")
+        direct = max(direct, err_A(host(Aw[0, h]), A_ref, "bf16"), err(host(Bw[0, h]), B_ref, "bf16"))
+        composed = max(composed, err_A(host(A12[h]), A_ref, "bf16"), err(host(B12[h]), B_ref, "bf16"))
+    print(f"map of the concatenation: err {direct:.3e}; composed from the two maps: err {composed:.3e}")
+    # each factor is within tol of its reference and has norm <= 1, so the composition (one more
+    # fp32 product) is within the sum of the two factors' errors
+    assert direct <= tol("bf16") and composed <= 2 * tol("bf16")
 
 
 def run_segmented(inp, seg_lengths):
