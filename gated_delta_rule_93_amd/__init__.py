@@ -79,6 +79,10 @@ def lib():
         L.kda_attnres_inter.restype = I
         L.kda_attnres_merge.argtypes = [I, I, I, P, P, F, P, P, P, P]
         L.kda_attnres_merge.restype = I
+        L.kda_fwd_chunk_local_scalar_gate.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, P, S, P]
+        L.kda_fwd_chunk_local_scalar_gate.restype = I
+        L.kda_fwd_chunk_local_lowrank_gate.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, I, P, P, P, P, S, P]
+        L.kda_fwd_chunk_local_lowrank_gate.restype = I
         L.kda_fwd_segment_map.argtypes = [I, I, I, I, I, I, P, I, P, P, P, S, P]
         L.kda_fwd_segment_map.restype = I
         L.kda_state_combine.argtypes = [I, I, I, P, P, P, P, P]
@@ -247,8 +251,12 @@ def _fwd(kind, q, k, v, g, beta, scale, initial_state, cu_seqlens, output_final_
     return o, final_state
 
 
-def fwd_chunk_local(q, k, v, g, beta, cu_seqlens=None, workspace=None, stream=None):
-    """First phase of kda_fwd (kda_fwd_chunk_local): the chunk records, into `workspace` (returned)."""
+def fwd_chunk_local(q, k, v, g, beta, cu_seqlens=None, workspace=None, stream=None, gate="channel",
+                    lowrank=None):
+    """First phase of the prefill: the chunk records, into `workspace` (returned).
+    gate "channel" (kda_fwd_chunk_local, g [B, T, H, dk]), "scalar" (kda_fwd_chunk_local_scalar_gate,
+    g [B, T, H] or None) or "lowrank" (kda_fwd_chunk_local_lowrank_gate, g None and
+    lowrank = (z, w_up, b_gate)).  The records feed fwd_state_scan and fwd_segment_map alike."""
     torch = _torch()
     io = _io_dtype(q)
     B, T, H, dk = q.shape
@@ -256,15 +264,33 @@ def fwd_chunk_local(q, k, v, g, beta, cu_seqlens=None, workspace=None, stream=No
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (B, T, H, dk))
     _need(v, "v", q.dtype, (B, T, H, dk))
-    _need(g, "g", torch.float32, (B, T, H, dk))
+    if gate == "channel":
+        _need(g, "g", torch.float32, (B, T, H, dk))
+    elif gate == "scalar":
+        if g is not None:
+            _need(g, "g", torch.float32, (B, T, H))
+    elif gate == "lowrank":
+        z, w_up, b_gate = lowrank
+        r = z.shape[-1]
+        _need(z, "z", torch.bfloat16, (B, T, r))
+        _need(w_up, "w_up", torch.bfloat16, (H * dk, r))
+        _need(b_gate, "b_gate", torch.float32, (H * dk,))
+    else:
+        raise ValueError(f"unknown gate form {gate!r}")
     _need(beta, "beta", torch.float32, (B, T, H))
     if cu_seqlens is not None:
         _need(cu_seqlens, "cu_seqlens", torch.int32)
     need = fwd_workspace_bytes(io, B, T, H, dk, dk, N, cu_seqlens is not None)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    _check(lib().kda_fwd_chunk_local(io, B, T, H, dk, dk, _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(g), _ptr(beta), _ptr(workspace), workspace.numel(), _stream(stream)))
+    head = (io, B, T, H, dk, dk, _ptr(cu_seqlens), N, _ptr(q), _ptr(k), _ptr(v))
+    tail = (_ptr(beta), _ptr(workspace), workspace.numel(), _stream(stream))
+    if gate == "channel":
+        _check(lib().kda_fwd_chunk_local(*head, _ptr(g), *tail))
+    elif gate == "scalar":
+        _check(lib().kda_fwd_chunk_local_scalar_gate(*head, _ptr(g), *tail))
+    else:
+        _check(lib().kda_fwd_chunk_local_lowrank_gate(*head, _ptr(z), r, _ptr(w_up), _ptr(b_gate), *tail))
     return workspace
 
 
@@ -327,20 +353,24 @@ def state_combine(transition, state_in, offset=None, out=None, stream=None):
     return out
 
 
-def fwd_segmented(q, k, v, g, beta, seg_bounds, scale: float = 1.0, initial_state=None, stream=None):
+def fwd_segmented(q, k, v, g, beta, seg_bounds, scale: float = 1.0, initial_state=None, stream=None,
+                  gate="channel", lowrank=None):
     """One sequence (B = 1) split at `seg_bounds` (int32 device tensor [P + 1], 0 .. T) into P
     segments and run as a context-parallel job would run it, here on one device: the chunk
     records and the affine map of every segment (all segments at once), the P - 1 hops of the
     prefix over segments (kda_state_combine, serial), then the state scan of every segment from
-    its incoming state.  Returns (o [1, T, H, dk], final_state [1, H, dk, dk], transition,
-    offset, incoming states [P, H, dk, dk])."""
+    its incoming state.  `gate` and `lowrank` select the gate form as in fwd_chunk_local.
+    Returns (o [1, T, H, dk], final_state [1, H, dk, dk], transition, offset, incoming states
+    [P, H, dk, dk])."""
     torch = _torch()
     io = _io_dtype(q)
     B, T, H, dk = q.shape
     if B != 1:
         raise ValueError("fwd_segmented takes one sequence (B = 1)")
     P = seg_bounds.numel() - 1
-    ws = fwd_chunk_local(q, k, v, g, beta, seg_bounds, stream=stream)
+    if P < 1:
+        raise ValueError("seg_bounds needs at least two entries (one segment)")
+    ws = fwd_chunk_local(q, k, v, g, beta, seg_bounds, stream=stream, gate=gate, lowrank=lowrank)
     A, Bm = fwd_segment_map(ws, io, 1, T, H, dk, seg_bounds, stream=stream)
     S_in = torch.empty((P, H, dk, dk), dtype=torch.float32, device=q.device)
     if initial_state is None:

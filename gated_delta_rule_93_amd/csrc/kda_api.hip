@@ -81,6 +81,20 @@ kda_status_t check_fwd(int part, kda_dtype_t io, int B, int T, int H, int d_k, i
     return KDA_OK;
 }
 
+// Checks of the low-rank gate operands shared by the fused forward and its chunk-local phase
+// (after check_fwd).
+kda_status_t check_lowrank(kda_dtype_t io, int B, int T, int N, int H, const void *z, int r, const void *w_up,
+                           const float *b_gate) {
+    if (r <= 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (io != KDA_BF16 || r % 32 != 0 || r > 128) return KDA_ERR_UNSUPPORTED;
+    if ((long)N * H == 0) return KDA_OK;
+    if ((long)B * T > 0) {
+        if (!z || !w_up || !b_gate) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned16(z) || !aligned16(w_up) || !aligned16(b_gate)) return KDA_ERR_INVALID_ARGUMENT;
+    }
+    return KDA_OK;
+}
+
 kda::FwdArgs fwd_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens, int N,
                       const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
                       const float *s0, float *sN, void *o, void *workspace) {
@@ -132,13 +146,8 @@ kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, 
     kda_status_t st = check_fwd(kBoth, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, nullptr, beta, initial_state,
                                 final_state, o, workspace, workspace_bytes, true);
     if (st != KDA_OK) return st;
-    if (r <= 0) return KDA_ERR_INVALID_ARGUMENT;
-    if (io != KDA_BF16 || r % 32 != 0 || r > 128) return KDA_ERR_UNSUPPORTED;
-    if ((long)N * H == 0) return KDA_OK;
-    if ((long)B * T > 0) {
-        if (!z || !w_up || !b_gate) return KDA_ERR_INVALID_ARGUMENT;
-        if (!aligned16(z) || !aligned16(w_up) || !aligned16(b_gate)) return KDA_ERR_INVALID_ARGUMENT;
-    }
+    st = check_lowrank(io, B, T, N, H, z, r, w_up, b_gate);
+    if (st != KDA_OK || (long)N * H == 0) return st;
     kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, nullptr, beta, scale, initial_state,
                               final_state, o, workspace);
     a.gate_z = static_cast<const uint16_t *>(z);
@@ -264,6 +273,38 @@ kda_status_t kda_fwd_state_scan(kda_dtype_t io, int B, int T, int H, int d_k, in
     const kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, nullptr, nullptr, nullptr, nullptr,
                                     nullptr, scale, initial_state, final_state, o, workspace);
     return kda::launch_fwd_scan(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_fwd_chunk_local_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                             const int32_t *cu_seqlens, int N, const void *q, const void *k,
+                                             const void *v, const float *g, const float *beta, void *workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+    kda_status_t st = check_fwd(kLocal, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, nullptr, nullptr,
+                                nullptr, workspace, workspace_bytes, true);
+    if (st != KDA_OK || (long)N * H == 0) return st;
+    kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, 1.f, nullptr, nullptr,
+                              nullptr, workspace);
+    a.scalar_gate = true;
+    return kda::launch_fwd_local(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+}
+
+kda_status_t kda_fwd_chunk_local_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                              const int32_t *cu_seqlens, int N, const void *q, const void *k,
+                                              const void *v, const void *z, int r, const void *w_up,
+                                              const float *b_gate, const float *beta, void *workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+    kda_status_t st = check_fwd(kLocal, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, nullptr, beta, nullptr,
+                                nullptr, nullptr, workspace, workspace_bytes, true);
+    if (st != KDA_OK) return st;
+    st = check_lowrank(io, B, T, N, H, z, r, w_up, b_gate);
+    if (st != KDA_OK || (long)N * H == 0) return st;
+    kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, nullptr, beta, 1.f, nullptr, nullptr,
+                              nullptr, workspace);
+    a.gate_z = static_cast<const uint16_t *>(z);
+    a.gate_w_up = static_cast<const uint16_t *>(w_up);
+    a.gate_b = b_gate;
+    a.gate_r = r;
+    return kda::launch_fwd_local(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_fwd_segment_map(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,

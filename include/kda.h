@@ -137,6 +137,19 @@ kda_status_t kda_fwd_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, i
                                  hipStream_t stream);
 
 /*
+ * kda_fwd_chunk_local_scalar_gate -- the chunk-local phase of kda_fwd_scalar_gate alone (same
+ * arguments, g [B, T, H] or NULL).  Its workspace records have the layout of kda_fwd_chunk_local's,
+ * so kda_fwd_state_scan and kda_fwd_segment_map take them: kda_fwd_scalar_gate(...) is exactly
+ * this call followed by kda_fwd_state_scan(...) on the same stream and workspace.
+ */
+kda_status_t kda_fwd_chunk_local_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                             const int32_t *cu_seqlens, int N,
+                                             const void *q, const void *k, const void *v,
+                                             const float *g, const float *beta,
+                                             void *workspace, size_t workspace_bytes,
+                                             hipStream_t stream);
+
+/*
  * Low-rank gate.  The page "Kimi K3 注意力三件套" (KDA section) says the per-channel alpha comes
  * from a low-rank down-up projection of the layer input x, and beta is one scalar; blog post-114
  * has beta = sigmoid(w_beta(x)) (chapter 3) and a gate per head and channel computed from x
@@ -183,6 +196,19 @@ kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, 
                                   const float *initial_state, float *final_state,
                                   void *o, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream);
+
+/*
+ * kda_fwd_chunk_local_lowrank_gate -- the chunk-local phase of kda_fwd_lowrank_gate alone (same
+ * arguments and checks).  As for kda_fwd_chunk_local_scalar_gate, its records feed
+ * kda_fwd_state_scan and kda_fwd_segment_map, and kda_fwd_lowrank_gate(...) is exactly this call
+ * followed by kda_fwd_state_scan(...).
+ */
+kda_status_t kda_fwd_chunk_local_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                              const int32_t *cu_seqlens, int N,
+                                              const void *q, const void *k, const void *v,
+                                              const void *z, int r, const void *w_up, const float *b_gate,
+                                              const float *beta, void *workspace, size_t workspace_bytes,
+                                              hipStream_t stream);
 
 /*
  * Segment maps (context parallelism).  Blog post-114, chapter 3: the chunked form computes

@@ -302,3 +302,25 @@ def test_state_combine_offset_checks():
     # the offset may be NULL (taken as zero; exercised on the GPU), but when given it is checked
     assert combine_call(Bm=FAKE + 4, count=0) == kda.KDA_OK       # count 0: nothing checked
     assert combine_call(Bm=FAKE + 4) == kda.KDA_ERR_INVALID_ARGUMENT  # misaligned offset
+
+
+def test_chunk_local_gate_forms_reject():
+    L = kda.lib()
+    # scalar gate: g may be NULL, beta may not; misaligned g; unsupported d
+    assert L.kda_fwd_chunk_local_scalar_gate(kda.KDA_BF16, 1, 64, 1, 128, 128, None, 1, FAKE, FAKE, FAKE, None,
+                                             None, FAKE, 1 << 30, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_fwd_chunk_local_scalar_gate(kda.KDA_BF16, 1, 64, 1, 128, 128, None, 1, FAKE, FAKE, FAKE,
+                                             FAKE + 4, FAKE, FAKE, 1 << 30, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert L.kda_fwd_chunk_local_scalar_gate(kda.KDA_BF16, 1, 64, 1, 96, 96, None, 1, FAKE, FAKE, FAKE, None,
+                                             FAKE, FAKE, 1 << 30, None) == kda.KDA_ERR_UNSUPPORTED
+    assert L.kda_fwd_chunk_local_scalar_gate(kda.KDA_BF16, 1, 64, 1, 128, 128, None, 1, FAKE, FAKE, FAKE, None,
+                                             FAKE, None, 0, None) == kda.KDA_ERR_WORKSPACE
+    # low-rank gate: rank, dtype and operand checks as for kda_fwd_lowrank_gate
+    lr = lambda **o: L.kda_fwd_chunk_local_lowrank_gate(
+        o.get("io", kda.KDA_BF16), 1, 64, 1, 128, 128, None, 1, FAKE, FAKE, FAKE, o.get("z", FAKE),
+        o.get("r", 32), o.get("w_up", FAKE), o.get("b", FAKE), FAKE, FAKE, 1 << 30, None)
+    assert lr(r=0) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lr(r=48) == kda.KDA_ERR_UNSUPPORTED
+    assert lr(io=kda.KDA_F32) == kda.KDA_ERR_UNSUPPORTED
+    assert lr(z=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lr(w_up=FAKE + 2) == kda.KDA_ERR_INVALID_ARGUMENT

@@ -198,3 +198,66 @@ def test_segmented_long_context_p8_sampled():
     tokens, one per device of an 8-way split; sampled heads checked in full."""
     inp = ki.config2()
     check_segmented(inp, [16384] * 8, "T=131072 P=8", heads=[0, 19, 31])
+
+
+def _phases_equal_fused(kind):
+    """kda_fwd_chunk_local_<kind>_gate + kda_fwd_state_scan is bitwise the fused entry point."""
+    if kind == "scalar":
+        inp = ki.make_scalar_gate([300], 2, 128, "bf16", 93230, dense_B=2)
+        q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
+        g, beta, S0 = dev_f32(inp.g), dev_f32(inp.beta), dev_f32(inp.S0)
+        o1, S1 = kda.fwd_scalar_gate(q, k, v, g, beta, 1.0, S0)
+        ws = kda.fwd_chunk_local(q, k, v, g, beta, gate="scalar")
+        B, T, H, d = inp.q.shape
+    else:
+        inp = ki.make_lowrank(2, 300, 2, 128, 32, 93231)
+        q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
+        lr = (dev_io(inp.z, "bf16"), dev_io(inp.w_up, "bf16"), dev_f32(inp.b))
+        beta, S0 = dev_f32(inp.beta), dev_f32(inp.S0)
+        o1, S1 = kda.fwd_lowrank_gate(q, k, v, *lr, beta, 1.0, S0)
+        ws = kda.fwd_chunk_local(q, k, v, None, beta, gate="lowrank", lowrank=lr)
+        B, T, H, d = inp.q.shape
+    o2, S2 = kda.fwd_state_scan(ws, kda.KDA_BF16, B, T, H, d, None, 1.0, S0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("kind", ["scalar", "lowrank"])
+def test_chunk_local_phase_of_each_gate_form_is_the_fused_call(kind):
+    _phases_equal_fused(kind)
+
+
+def test_segmented_scalar_gate():
+    """One decay per token and head, one sequence in 3 segments, against the oracle over the
+    unsplit sequence (the decay copied to every key channel)."""
+    inp = ki.make_scalar_gate([1500], 3, 128, "bf16", 93232, dense_B=1, g_shift=-5.0)
+    q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    cu = torch.from_numpy(_bounds([512, 700, 288]).astype(np.int32)).to(DEV)
+    o, S, _, _, _ = kda.fwd_segmented(q, k, v, dev_f32(inp.g), dev_f32(inp.beta), cu, 1.0, dev_f32(inp.S0),
+                                      gate="scalar")
+    torch.cuda.synchronize()
+    gb = ki.broadcast_gate(inp.g, inp.q)
+    res = oracle.Recurrence(inp.q, inp.k, inp.v, gb, inp.beta, 1.0, inp.S0).run()
+    e_o = max(err(host(o[0, :, h]), o_ref, "bf16") for (_, h), (o_ref, _) in res.items())
+    e_s = max(err(host(S[0, h]), S_ref, "bf16") for (_, h), (_, S_ref) in res.items())
+    print(f"segmented scalar gate: o err {e_o:.3e}, state err {e_s:.3e}")
+    assert e_o <= tol("bf16") and e_s <= tol("bf16")
+
+
+def test_segmented_lowrank_gate():
+    """The gate in low-rank form (log alpha formed inside the chunk-local kernel), one sequence in
+    4 segments, against the oracle over the unsplit sequence with g from the oracle's gate."""
+    inp = ki.make_lowrank(1, 1200, 2, 128, 32, 93233, b_mean=-5.0)
+    q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    lr = (dev_io(inp.z, "bf16"), dev_io(inp.w_up, "bf16"), dev_f32(inp.b))
+    cu = torch.from_numpy(_bounds([256, 333, 400, 211]).astype(np.int32)).to(DEV)
+    o, S, _, _, _ = kda.fwd_segmented(q, k, v, None, dev_f32(inp.beta), cu, 1.0, dev_f32(inp.S0),
+                                      gate="lowrank", lowrank=lr)
+    torch.cuda.synchronize()
+    B, T, H, d = inp.q.shape
+    g = oracle.gate_g(inp.z.reshape(B * T, -1), inp.w_up, inp.b, H, d).reshape(B, T, H, d)
+    res = oracle.Recurrence(inp.q, inp.k, inp.v, g, inp.beta, 1.0, inp.S0).run()
+    e_o = max(err(host(o[0, :, h]), o_ref, "bf16") for (_, h), (o_ref, _) in res.items())
+    e_s = max(err(host(S[0, h]), S_ref, "bf16") for (_, h), (_, S_ref) in res.items())
+    print(f"segmented low-rank gate: o err {e_o:.3e}, state err {e_s:.3e}")
+    assert e_o <= tol("bf16") and e_s <= tol("bf16")
