@@ -8,7 +8,9 @@
 //
 // HBM-bound stencil.  Each thread owns 8 consecutive channels (one 16-byte bf16 vector) of one
 // head and walks TT consecutive tokens, keeping the W-1 previous inputs in registers, so the
-// input is read once plus a (W-1)/TT halo.  The d/8 lanes of a head reduce the sum of squares
+// input is read once plus a (W-1)/TT halo.  The rows of the next kPrepPF tokens are always in
+// flight (a ring of raw 16-byte vectors): with one row per wave in flight the kernel was bound
+// by load latency.  The d/8 lanes of a head reduce the sum of squares
 // with xor shuffles inside their aligned lane group (fixed order, deterministic).  SiLU and the
 // norm use the hardware reciprocal and reciprocal square root (about 1 ulp each): the division
 // and square root of IEEE fp32 made the kernel issue-bound at 3.7 TB/s.  bf16 rows are read and
@@ -18,14 +20,18 @@
 
 namespace kda {
 
-constexpr int kPrepTT = 32;
+constexpr int kPrepTT = 64;
+constexpr int kPrepPF = 4;  // token rows in flight per thread
+static_assert(kPrepTT % kPrepPF == 0, "whole prefetch groups per block");
 
 template <typename TIO> struct Vec8;
 template <> struct Vec8<uint16_t> {
-    static __device__ __forceinline__ void load(const uint16_t *p, float *x) {
-        typedef __attribute__((ext_vector_type(4))) unsigned int v4u;
-        const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u *>(p));
-        uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    typedef __attribute__((ext_vector_type(4))) unsigned int Raw;
+    static __device__ __forceinline__ Raw load_raw(const uint16_t *p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const Raw *>(p));
+    }
+    static __device__ __forceinline__ void unpack(const Raw &w, float *x) {
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = __uint_as_float(u[i] << 16);
@@ -33,20 +39,22 @@ template <> struct Vec8<uint16_t> {
         }
     }
     static __device__ __forceinline__ void store(uint16_t *p, const float *x) {
-        typedef __attribute__((ext_vector_type(4))) unsigned int v4u;
-        v4u w;
+        Raw w;
         w.x = pack_bf16x2(x[0], x[1]);
         w.y = pack_bf16x2(x[2], x[3]);
         w.z = pack_bf16x2(x[4], x[5]);
         w.w = pack_bf16x2(x[6], x[7]);
-        __builtin_nontemporal_store(w, reinterpret_cast<v4u *>(p));
+        __builtin_nontemporal_store(w, reinterpret_cast<Raw *>(p));
     }
 };
 template <> struct Vec8<float> {
-    static __device__ __forceinline__ void load(const float *p, float *x) {
-        f32x4 a = reinterpret_cast<const f32x4 *>(p)[0], b = reinterpret_cast<const f32x4 *>(p)[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    struct Raw { f32x4 a, b; };
+    static __device__ __forceinline__ Raw load_raw(const float *p) {
+        return Raw{reinterpret_cast<const f32x4 *>(p)[0], reinterpret_cast<const f32x4 *>(p)[1]};
+    }
+    static __device__ __forceinline__ void unpack(const Raw &w, float *x) {
+        x[0] = w.a.x; x[1] = w.a.y; x[2] = w.a.z; x[3] = w.a.w;
+        x[4] = w.b.x; x[5] = w.b.y; x[6] = w.b.z; x[7] = w.b.w;
     }
     static __device__ __forceinline__ void store(float *p, const float *x) {
         reinterpret_cast<f32x4 *>(p)[0] = f32x4{x[0], x[1], x[2], x[3]};
@@ -96,62 +104,83 @@ prep_kernel(const TIO *__restrict__ x, const float *__restrict__ w, TIO *__restr
         seq_start = (t0 / T) * T;
         seq_end = seq_start + T;
     }
-    // history: hist[m] holds token t - (W-1) + m for the next t
+    // history: hist[m] holds token t - (W-1) + m for the next t.  Every load below reads a valid
+    // row (tokens before 0 or past t1 - 1 are clamped into [0, t1 - 1] and the values then
+    // replaced or never used; threads of a head past H read head 0), so all of them are issued
+    // without branches and stay in flight together.
+    using Raw = typename Vec8<TIO>::Raw;
+    const TIO *xc0 = x + c0;
     float hist[W > 1 ? W - 1 : 1][8];
+    {
+        Raw hr[W > 1 ? W - 1 : 1];
 #pragma unroll
-    for (int m = 0; m < W - 1; ++m) {
-        const long ts = t0 - (W - 1) + m;
-        if (active && ts >= seq_start) Vec8<TIO>::load(x + ts * row + c0, hist[m]);
-        else {
+        for (int m = 0; m < W - 1; ++m) {
+            const long ts = t0 - (W - 1) + m;
+            hr[m] = Vec8<TIO>::load_raw(xc0 + (ts >= 0 ? ts : t0) * row);
+        }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hist[m][j] = 0.f;
+        for (int m = 0; m < W - 1; ++m) {
+            const long ts = t0 - (W - 1) + m;
+            const bool live = active && ts >= seq_start;
+            Vec8<TIO>::unpack(hr[m], hist[m]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hist[m][j] = live ? hist[m][j] : 0.f;
         }
     }
-    for (long t = t0; t < t1; ++t) {
-        while (t >= seq_end && (!cu || n + 1 < N)) {  // crossed into the next sequence: zero history
-            if (cu) {
-                ++n;
-                seq_start = cu[n];
-                seq_end = cu[n + 1];
-            } else {
-                seq_start = seq_end;
-                seq_end = seq_start + T;
+    Raw pend[kPrepPF];  // pend[j]: the row of token tb + j of the current group
+#pragma unroll
+    for (int j = 0; j < kPrepPF; ++j) pend[j] = Vec8<TIO>::load_raw(xc0 + min(t0 + j, t1 - 1) * row);
+    for (long tb = t0; tb < t1; tb += kPrepPF) {
+#pragma unroll
+        for (int j = 0; j < kPrepPF; ++j) {
+            // tokens past t1 - 1 (only in a block's last group, for the last block) are computed
+            // from clamped rows and not stored: no branch around the ring, whose registers then
+            // stay fixed and are never copied while a load into them is in flight
+            const long t = tb + j;
+            float xc[8];
+            Vec8<TIO>::unpack(pend[j], xc);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xc[i] = active ? xc[i] : 0.f;  // a select, not a branch
+            pend[j] = Vec8<TIO>::load_raw(xc0 + min(t + kPrepPF, t1 - 1) * row);  // token t + kPrepPF
+            while (t >= seq_end && (!cu || n + 1 < N)) {  // crossed into the next sequence: zero history
+                if (cu) {
+                    ++n;
+                    seq_start = cu[n];
+                    seq_end = cu[n + 1];
+                } else {
+                    seq_start = seq_end;
+                    seq_end = seq_start + T;
+                }
+#pragma unroll
+                for (int m = 0; m < W - 1; ++m)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) hist[m][i] = 0.f;
+            }
+            float yv[8];
+            float ss = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float c = wt[i][W - 1] * xc[i];
+#pragma unroll
+                for (int m = 0; m < W - 1; ++m) c = fmaf(wt[i][m], hist[m][i], c);
+                const float s = c * __builtin_amdgcn_rcpf(1.f + fast_exp2(-c * kLog2e));
+                yv[i] = s;
+                ss = fmaf(s, s, ss);
             }
 #pragma unroll
-            for (int m = 0; m < W - 1; ++m)
+            for (int off = LPH / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+            const float inv = ss > 1e-24f ? __builtin_amdgcn_rsqf(ss) : 1e12f;  // 1 / max(||y||, 1e-12)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) hist[m][j] = 0.f;
-        }
-        float xc[8];
-        if (active) Vec8<TIO>::load(x + t * row + c0, xc);
-        else {
+            for (int i = 0; i < 8; ++i) yv[i] *= inv;
+            if (active && t < t1) Vec8<TIO>::store(y + t * row + c0, yv);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xc[j] = 0.f;
-        }
-        float yv[8];
-        float ss = 0.f;
+            for (int m = 0; m + 1 < W - 1; ++m)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float c = wt[j][W - 1] * xc[j];
+                for (int i = 0; i < 8; ++i) hist[m][i] = hist[m + 1][i];
+            if (W > 1) {
 #pragma unroll
-            for (int m = 0; m < W - 1; ++m) c = fmaf(wt[j][m], hist[m][j], c);
-            const float s = c * __builtin_amdgcn_rcpf(1.f + fast_exp2(-c * kLog2e));
-            yv[j] = s;
-            ss = fmaf(s, s, ss);
-        }
-#pragma unroll
-        for (int off = LPH / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-        const float inv = ss > 1e-24f ? __builtin_amdgcn_rsqf(ss) : 1e12f;  // 1 / max(||y||, 1e-12)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) yv[j] *= inv;
-        if (active) Vec8<TIO>::store(y + t * row + c0, yv);
-#pragma unroll
-        for (int m = 0; m + 1 < W - 1; ++m)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) hist[m][j] = hist[m + 1][j];
-        if (W > 1) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) hist[W > 1 ? W - 2 : 0][j] = xc[j];
+                for (int i = 0; i < 8; ++i) hist[W > 1 ? W - 2 : 0][i] = xc[i];
+            }
         }
     }
 }
