@@ -677,7 +677,11 @@ def main():
         log("prep ...")
         pr = bench_prep(args, torch, kda, dev)
         out["prep"] = {"workload": f"{pr['tokens']} packed tokens (64 sequences), H=32, d=128, width 4, bf16",
-                       "ms": pr["ms"], "GBs": pr["gbs"], "frac": pr["gbs"] / HBM_PEAK_GBS}
+                       "ms": pr["ms"], "GBs": pr["gbs"], "frac": pr["gbs"] / HBM_PEAK_GBS,
+                       "roofline": {"bound": "hbm", "kernel": "prep_kernel", "achieved": pr["gbs"], "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": pr["gbs"] / HBM_PEAK_GBS,
+                                    "algorithmic_bytes_per_launch": pr["bytes"],
+                                    "traffic": measured_traffic("prep_kernel")}}
     if "scalar" in only:
         log("scalar gate ...")
         out["scalar_gate"] = bench_scalar_gate(torch, kda, dev)
