@@ -47,3 +47,17 @@ def test_prep_config4_shape_sampled():
         ref = oracle.prep_sequence(x[0, cu[n]:cu[n + 1]].reshape(-1, H * d), w, H, d)
         e = err(host(y[0, cu[n]:cu[n + 1]]).reshape(-1, H * d), ref, "bf16")
         assert e <= tol("bf16"), (n, e)
+
+
+def test_prep_many_short_sequences():
+    """Blocks of 64 tokens that cross dozens of sequence starts (lengths 0..3), a ragged last block,
+    and a head count that leaves most threads of the second head group idle."""
+    lengths = [(3 * i) % 4 for i in range(150)]
+    H, d = 17, 128
+    x, w, cu = ki.prep_inputs(lengths, H, d, "bf16", 4711, width=4)
+    y = kda.prep(dev_io(x, "bf16"), dev_f32(w), cu_seqlens=torch.from_numpy(cu).to(DEV))
+    ref = oracle.prep(x, w, cu, H, d)
+    ref_all = np.concatenate([ref[n] for n in range(len(lengths))])
+    e = err(host(y).reshape(-1, H * d), ref_all, "bf16")
+    print(f"prep, 150 sequences of 0..3 tokens ({cu[-1]} tokens), H=17: err {e:.3e}")
+    assert e <= tol("bf16")
