@@ -74,7 +74,7 @@ def time_events(fn, reps, torch):
 
 def bench_prefill(args, torch, kda, dev):
     import kda_inputs as ki
-    inp = ki.config1()
+    inp = ki.prefill_batch()
     B, T, H, d = inp.B, inp.T, inp.H, inp.dk
     q, k, v = (bf16_dev(x, dev) for x in (inp.q, inp.k, inp.v))
     g = torch.from_numpy(inp.g).to(dev)
@@ -172,7 +172,7 @@ def bench_decode(args, torch, kda, dev):
 
 def bench_prep(args, torch, kda, dev):
     import kda_inputs as ki
-    lengths = ki.config4_lengths()
+    lengths = ki.varlen_layer_lengths()
     H, d = 32, 128
     cu = np.zeros(len(lengths) + 1, np.int32)
     cu[1:] = np.cumsum(lengths)
@@ -460,7 +460,7 @@ def bench_varlen_layer(torch, kda, dev, reps=5):
     """Varlen layer: 64 packed sequences (lengths U[512, 16384] from the workload seed), H=32, d=128:
     prologue on raw q and k (width 4), then the chunked prefill with per-sequence S_0 ~ N(0, 0.02)."""
     import kda_inputs as ki
-    lengths = ki.config4_lengths()
+    lengths = ki.varlen_layer_lengths()
     H, d = 32, 128
     cu = np.zeros(len(lengths) + 1, np.int32)
     cu[1:] = np.cumsum(lengths)

@@ -236,43 +236,43 @@ def prep_inputs(lengths, H: int, d: int, io: str, seed: int, w_std: float = 0.5,
 
 
 # --------------------------------------------------------------------------- named workloads
-def config0() -> KDAInputs:
+def small_fp32() -> KDAInputs:
     """fp32 recurrence: B=1, H=2, T=256, d=64, S0 = 0."""
     return make_dense(1, 256, 2, 64, 64, "f32", SEED_BASE + 0)
 
 
-def config1() -> KDAInputs:
+def prefill_batch() -> KDAInputs:
     """Chunked prefill: B=4, H=16, T=4096, d=128, bf16 q/k/v, S0 = 0."""
     return make_dense(4, 4096, 16, 128, 128, "bf16", SEED_BASE + 1)
 
 
-def config2() -> KDAInputs:
+def long_context() -> KDAInputs:
     """Long-context prefill: B=1, H=32, T=131072, d=128, bf16 q/k/v, S0 ~ N(0, 0.02)."""
     return make_dense(1, 131072, 32, 128, 128, "bf16", SEED_BASE + 2, s0_std=0.02)
 
 
-CONFIG3 = dict(N=256, H=32, d=128, steps=100, seed=SEED_BASE + 3)
-CONFIG4 = dict(n_seq=64, lo=512, hi=16384, H=32, d=128, seed=SEED_BASE + 4)
+DECODE_POOL = dict(N=256, H=32, d=128, steps=100, seed=SEED_BASE + 3)
+VARLEN_LAYER = dict(n_seq=64, lo=512, hi=16384, H=32, d=128, seed=SEED_BASE + 4)
 
 
-def config4_lengths() -> np.ndarray:
-    return varlen_lengths(CONFIG4["n_seq"], CONFIG4["lo"], CONFIG4["hi"], CONFIG4["seed"])
+def varlen_layer_lengths() -> np.ndarray:
+    return varlen_lengths(VARLEN_LAYER["n_seq"], VARLEN_LAYER["lo"], VARLEN_LAYER["hi"], VARLEN_LAYER["seed"])
 
 
-def config4_sequence(n: int, H: int = 32, d: int = 128, g_shift: float = 2.0):
+def varlen_layer_sequence(n: int, H: int = 32, d: int = 128, g_shift: float = 2.0):
     """Sequence n of the varlen layer workload: raw q, k ~ N(0,1) (bf16, before the prologue),
     v ~ N(0,1) bf16, beta, g, and S_0 ~ N(0, 0.02), all from default_rng([seed, n])."""
-    L = int(config4_lengths()[n])
-    rng = np.random.default_rng([CONFIG4["seed"], n])
+    L = int(varlen_layer_lengths()[n])
+    rng = np.random.default_rng([VARLEN_LAYER["seed"], n])
     q, k, v, beta, g = draw_tokens(rng, (L,), H, d, d, "bf16", g_shift, normalize_qk=False)
     S0 = rng.standard_normal((H, d, d), dtype=np.float32) * np.float32(0.02)
     return q, k, v, beta, g, S0
 
 
-def config4_conv_weights(H: int = 32, d: int = 128, width: int = 4):
+def varlen_layer_conv_weights(H: int = 32, d: int = 128, width: int = 4):
     """w_q, w_k [H*d, width] ~ N(0, 0.5), drawn after the lengths from the workload seed."""
-    rng = np.random.default_rng(CONFIG4["seed"])
-    rng.integers(CONFIG4["lo"], CONFIG4["hi"], size=CONFIG4["n_seq"], endpoint=True)
+    rng = np.random.default_rng(VARLEN_LAYER["seed"])
+    rng.integers(VARLEN_LAYER["lo"], VARLEN_LAYER["hi"], size=VARLEN_LAYER["n_seq"], endpoint=True)
     wq = rng.standard_normal((H * d, width), dtype=np.float32) * np.float32(0.5)
     wk = rng.standard_normal((H * d, width), dtype=np.float32) * np.float32(0.5)
     return wq, wk

@@ -11,10 +11,10 @@ from gpu_util import DEV, dev_f32, dev_io, err, host, tol
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_config3_sampled_chains():
+def test_decode_pool_256x32_sampled_chains():
     """256 sequences x 32 heads, d = 128, bf16 tokens, fp32 state in HBM, 100 steps.
     All heads run on the GPU; 48 sampled (sequence, head) chains are checked step by step."""
-    c = ki.CONFIG3
+    c = ki.DECODE_POOL
     N, H, d, steps, seed = c["N"], c["H"], c["d"], c["steps"], c["seed"]
     S0 = ki.decode_initial_state(N, H, d, seed)
     state = dev_f32(S0)
@@ -37,13 +37,13 @@ def test_decode_config3_sampled_chains():
                                     np.stack(rec["g"]), np.array(rec["b"]), 1.0, S0[n, h])
         worst_o = max(worst_o, err(np.stack(rec["o"]), o_ref, "bf16"))
         worst_s = max(worst_s, err(S_gpu[n, h], S_ref, "bf16"))
-    print(f"decode config3: o err {worst_o:.3e}, state err {worst_s:.3e}")
+    print(f"decode 256 x 32 heads: o err {worst_o:.3e}, state err {worst_s:.3e}")
     assert worst_o <= tol("bf16") and worst_s <= tol("bf16")
 
 
-def test_decode_fp32_equals_recurrence_config0():
-    """Config 0 (fp32, d = 64, T = 256) run as 256 consecutive decode steps."""
-    inp = ki.config0()
+def test_decode_fp32_equals_recurrence_small():
+    """The small fp32 workload (B = 1, H = 2, T = 256, d = 64) run as 256 consecutive decode steps."""
+    inp = ki.small_fp32()
     o_ref, S_ref = oracle.recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
     state = torch.zeros((1, inp.H, 64, 64), dtype=torch.float32, device=DEV)
     outs = []
@@ -53,7 +53,7 @@ def test_decode_fp32_equals_recurrence_config0():
         outs.append(host(o))
     o_gpu = np.stack(outs, axis=1)
     e_o, e_s = err(o_gpu, o_ref, "f32"), err(host(state), S_ref, "f32")
-    print(f"decode config0 fp32: o err {e_o:.3e}, state err {e_s:.3e}")
+    print(f"decode fp32 B1 H2 T256 d64: o err {e_o:.3e}, state err {e_s:.3e}")
     assert e_o <= tol("f32") and e_s <= tol("f32")
 
 

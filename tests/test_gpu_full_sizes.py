@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 def test_long_context_t131072_h32_sampled_heads():
     """B=1, H=32, T=131072, d=128, bf16 q/k/v, S_0 ~ N(0, 0.02): 2048 chunks per chain."""
-    inp = ki.config2()
+    inp = ki.long_context()
     q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
     o, S = kda.fwd(q, k, v, dev_f32(inp.g), dev_f32(inp.beta), 1.0, dev_f32(inp.S0))
     torch.cuda.synchronize()
@@ -32,7 +32,7 @@ def test_long_context_t131072_h32_sampled_heads():
 def test_varlen_layer_prep_then_fwd_sampled():
     """64 packed sequences, lengths U[512, 16384], H=32, d=128: raw q/k -> prologue (width 4)
     -> chunked prefill with per-sequence initial and final states."""
-    lengths = ki.config4_lengths()
+    lengths = ki.varlen_layer_lengths()
     H, d = 32, 128
     cu = np.zeros(len(lengths) + 1, np.int64)
     cu[1:] = np.cumsum(lengths)
@@ -45,17 +45,17 @@ def test_varlen_layer_prep_then_fwd_sampled():
     S0 = torch.empty((len(lengths), H, d, d), dtype=torch.float32, device=DEV)
     for n in range(len(lengths)):
         s, e = int(cu[n]), int(cu[n + 1])
-        qn, kn, vn, bn, gn, S0n = ki.config4_sequence(n, H, d)
+        qn, kn, vn, bn, gn, S0n = ki.varlen_layer_sequence(n, H, d)
         qr[0, s:e], kr[0, s:e], v[0, s:e] = dev_io(qn, "bf16"), dev_io(kn, "bf16"), dev_io(vn, "bf16")
         g[0, s:e], beta[0, s:e], S0[n] = dev_f32(gn), dev_f32(bn), dev_f32(S0n)
-    wq, wk = ki.config4_conv_weights(H, d)
+    wq, wk = ki.varlen_layer_conv_weights(H, d)
     cu_d = torch.from_numpy(cu.astype(np.int32)).to(DEV)
     q = kda.prep(qr, dev_f32(wq), cu_d)
     k = kda.prep(kr, dev_f32(wk), cu_d)
     o, S = kda.fwd(q, k, v, g, beta, 1.0, S0, cu_d)
     torch.cuda.synchronize()
     for n, h in ((0, 5), (23, 0), (63, 31)):
-        qn, kn, vn, bn, gn, S0n = ki.config4_sequence(n, H, d)
+        qn, kn, vn, bn, gn, S0n = ki.varlen_layer_sequence(n, H, d)
         L = qn.shape[0]
         qp = oracle.prep_sequence(qn.reshape(L, H * d), wq, H, d).reshape(L, H, d)
         kp = oracle.prep_sequence(kn.reshape(L, H * d), wk, H, d).reshape(L, H, d)

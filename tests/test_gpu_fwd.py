@@ -29,9 +29,9 @@ def run_and_check(inp: ki.KDAInputs, scale=1.0, chains=None, label=""):
     return o, S
 
 
-def test_fwd_config0_fp32():
+def test_fwd_small_fp32():
     """B=1, H=2, T=256, d=64, fp32, S0 = 0 (gate 1e-4)."""
-    run_and_check(ki.config0(), label="config0")
+    run_and_check(ki.small_fp32(), label="fp32 B1 H2 T256 d64")
 
 
 def test_fwd_small_bf16_ragged():
@@ -44,9 +44,9 @@ def test_fwd_other_dtypes_and_sizes(io, d):
     run_and_check(ki.make_dense(2, 150, 2, d, d, io, 12 + d, s0_std=0.3), label=f"{io} d={d}")
 
 
-def test_fwd_config1_full():
+def test_fwd_prefill_batch_full():
     """B=4, H=16, T=4096, d=128, bf16 q/k/v, fp32 g/beta/state, S0 = 0: every chain checked."""
-    run_and_check(ki.config1(), label="config1")
+    run_and_check(ki.prefill_batch(), label="bf16 B4 H16 T4096 d128")
 
 
 @pytest.mark.parametrize("variant", ["weak_decay", "alpha_one", "scalar_alpha"])

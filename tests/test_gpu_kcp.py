@@ -196,7 +196,7 @@ def test_segmented_zero_initial_state_and_empty_segments():
 def test_segmented_long_context_p8_sampled():
     """The long-context workload (B=1, H=32, T=131072, S_0 given) split into 8 segments of 16384
     tokens, one per device of an 8-way split; sampled heads checked in full."""
-    inp = ki.config2()
+    inp = ki.long_context()
     check_segmented(inp, [16384] * 8, "T=131072 P=8", heads=[0, 19, 31])
 
 

@@ -36,10 +36,10 @@ def test_prep_dense_rows_are_sequences():
         assert err(y[b].reshape(T, H * d), ref, "bf16") <= tol("bf16")
 
 
-def test_prep_config4_shape_sampled():
-    """Config-4 packing (64 sequences, lengths U[512, 16384], H = 32, d = 128, width 4): the whole
+def test_prep_varlen_layer_shape_sampled():
+    """The varlen layer packing (64 sequences, lengths U[512, 16384], H = 32, d = 128, width 4): the whole
     batch runs on the GPU, 4 sampled sequences are checked against the oracle."""
-    lengths = ki.config4_lengths()
+    lengths = ki.varlen_layer_lengths()
     H, d = 32, 128
     x, w, cu = ki.prep_inputs(lengths, H, d, "bf16", ki.SEED_BASE + 4)
     y = kda.prep(dev_io(x, "bf16"), dev_f32(w), cu_seqlens=torch.from_numpy(cu).to(DEV))

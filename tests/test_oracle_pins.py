@@ -75,7 +75,7 @@ def test_nan_propagates(chain_fn):
     assert np.isnan(o[2:]).any() and np.isnan(S).any() and not np.isnan(o[:2]).any()
 
 
-def test_gpu_factorisation_plan_is_exact_at_config_decay():
+def test_gpu_factorisation_plan_is_exact_at_workload_decay():
     """The sub-block factorisation and blocked inverse reproduce the recurrence in fp64 at the
     workload's decay strength (log-decay spans of ~140 per 64-token chunk), with a ragged tail."""
     import kda_inputs as ki
