@@ -11,6 +11,8 @@
 // per 16-token row tile.  z is rounded to bf16 once; the optional log(alpha) is formed from those
 // rounded values by the same MFMA and the same nonlinearity as the fused chunk-local kernel, so
 // the two paths agree bit for bit.
+#include <utility>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -37,6 +39,10 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + fast_e
 __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
     __shared__ uint16_t zs[kGateTokens][128 + 8];  // the block's rounded z rows (for log(alpha))
     __shared__ f32x4 red[4][4][64];                // upper-half partial sums of four column tiles
+    // whole-line path: each wave's 16 x rows and, shared by the four waves of a width half, the
+    // weight rows of the column group, 128 widths per step (+ 8 of padding against bank conflicts)
+    __shared__ __attribute__((aligned(16))) uint16_t xs[8][16][136];
+    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][2][4][16][136];  // [step parity][half][tile]
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     const int tt = wave & 3, kh = wave >> 2;
     const long tok0 = (long)blockIdx.x * kGateTokens;
@@ -49,6 +55,15 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
     // width is branch-free (every tile of the group is loaded from a valid row and masked), so
     // the unrolled iterations keep their loads in flight together.
     const uint16_t *xp = a.x + (long)xrow * a.Dm + 8 * grp;
+    // Whole-line path (the width a multiple of 256, so both halves have the same whole steps): load j
+    // of a wave covers rows 8 (j >> 1) + (l >> 3) and bytes 128 (j & 1) + 16 (l & 7) of each row's
+    // 256-byte step, so every request is a whole 128-byte line; the operands are then read from LDS
+    // in the fragment layout.  Loaded this way (the other path puts 16 rows x 64 bytes in one load),
+    // the kernel ran 35 -> 30 us on x alone.
+    const bool lines = (nkb & 7) == 0;  // uniform over the workgroup
+    const long lrow0 = tok0 + 16 * tt + (lane >> 3), lrow1 = lrow0 + 8;
+    const uint16_t *xl[2] = {a.x + (lrow0 < a.Ntok ? lrow0 : a.Ntok - 1) * (long)a.Dm + 8 * (lane & 7),
+                             a.x + (lrow1 < a.Ntok ? lrow1 : a.Ntok - 1) * (long)a.Dm + 8 * (lane & 7)};
     for (int cg = 0; cg < nct; cg += 4) {
         const uint16_t *wp[4];  // this lane's weight row of each tile of the group
         bool wvalid[4];         // false for rows past H (and tiles past the last): zero operand
@@ -61,6 +76,59 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
             wp[u] = (wvalid[u] ? (zt ? a.w_down : a.w_beta) + (long)row * a.Dm : a.w_down) + 8 * grp;
         }
         f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+        if (lines) {
+            // wave (tt, kh) stages weight tile cg + tt of half kh; rows past the valid ones read
+            // row 0 of w_down and are masked by the consumer (wvalid)
+            const int ctw = cg + tt;
+            const bool ztw = ctw < nzt;
+            const uint16_t *wl[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int rr = 8 * h2 + (lane >> 3);
+                const int row = ztw ? 16 * ctw + rr : 16 * (ctw - nzt) + rr;
+                const bool ok = ztw || (ctw < nct && row < a.H);
+                wl[h2] = (ok ? (ztw ? a.w_down : a.w_beta) + (long)row * a.Dm : a.w_down) + 8 * (lane & 7);
+            }
+            auto issue = [&](int kb, u32x4 (&xr)[4], u32x4 (&wr)[4]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    xr[j] = ld16(xl[j >> 1] + 32 * kb + 64 * (j & 1));
+                    wr[j] = ld16(wl[j >> 1] + 32 * kb + 64 * (j & 1));
+                }
+            };
+            // one step: the loads of the next step are already in flight (other register set)
+            auto consume = [&](auto bufc, u32x4 (&xr)[4], u32x4 (&wr)[4]) __attribute__((always_inline)) {
+                constexpr int buf = decltype(bufc)::value;
+                asm volatile("" : "+v"(xr[0]), "+v"(xr[1]), "+v"(xr[2]), "+v"(xr[3]),
+                                  "+v"(wr[0]), "+v"(wr[1]), "+v"(wr[2]), "+v"(wr[3]));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rr = 8 * (j >> 1) + (lane >> 3), cc = 64 * (j & 1) + 8 * (lane & 7);
+                    *reinterpret_cast<u32x4 *>(&xs[wave][rr][cc]) = xr[j];
+                    *reinterpret_cast<u32x4 *>(&wsh[buf][kh][tt][rr][cc]) = wr[j];
+                }
+                __syncthreads();  // the half's four weight tiles of this step are in LDS
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const FragB xa{__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xs[wave][r16][32 * i + 8 * grp]))};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const u32x4 w = *reinterpret_cast<const u32x4 *>(&wsh[buf][kh][u][r16][32 * i + 8 * grp]);
+                        acc[u] = mfma(xa, FragB{__builtin_bit_cast(bf16x8, wvalid[u] ? w : u32x4{0u, 0u, 0u, 0u})}, acc[u]);
+                    }
+                }
+            };
+            // Every load is unconditional (a step past the end reloads the last one), so the wait
+            // before each step counts exactly the loads of the step after it.
+            u32x4 xa0[4], wa0[4], xa1[4], wa1[4];
+            issue(kb0, xa0, wa0);
+            for (int kb = kb0; kb < kb1; kb += 8) {
+                issue(min(kb + 4, kb1 - 4), xa1, wa1);
+                consume(std::integral_constant<int, 0>{}, xa0, wa0);
+                issue(min(kb + 8, kb1 - 4), xa0, wa0);
+                if (kb + 4 < kb1) consume(std::integral_constant<int, 1>{}, xa1, wa1);
+            }
+        } else {
         // four k blocks per step: all 20 loads are issued before the 16 MFMAs that use them
         for (int kb = kb0; kb < kb1; kb += 4) {
             u32x4 xv[4], wv4[4][4];
@@ -89,6 +157,7 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
                     acc[u] = mfma(xa, FragB{__builtin_bit_cast(bf16x8, w)}, acc[u]);
                 }
             }
+        }
         }
         // add the two halves in a fixed order (lower + upper), so the result is deterministic
         if (kh == 1) {
