@@ -42,7 +42,11 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
     // whole-line path: each wave's 16 x rows and, shared by the four waves of a width half, the
     // weight rows of the column group, 128 widths per step (+ 8 of padding against bank conflicts)
     __shared__ __attribute__((aligned(16))) uint16_t xs[8][16][136];
-    __shared__ __attribute__((aligned(16))) uint16_t wsh[2][2][4][16][136];  // [step parity][half][tile]
+    // [step parity][half][tile] weight rows; afterwards, per wave, 16 rows x 128 columns of log(alpha)
+    __shared__ __attribute__((aligned(16))) union {
+        uint16_t w[2][2][4][16][136];
+        float g[8][16][132];
+    } stg;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     const int tt = wave & 3, kh = wave >> 2;
     const long tok0 = (long)blockIdx.x * kGateTokens;
@@ -105,7 +109,7 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
                 for (int j = 0; j < 4; ++j) {
                     const int rr = 8 * (j >> 1) + (lane >> 3), cc = 64 * (j & 1) + 8 * (lane & 7);
                     *reinterpret_cast<u32x4 *>(&xs[wave][rr][cc]) = xr[j];
-                    *reinterpret_cast<u32x4 *>(&wsh[buf][kh][tt][rr][cc]) = wr[j];
+                    *reinterpret_cast<u32x4 *>(&stg.w[buf][kh][tt][rr][cc]) = wr[j];
                 }
                 __syncthreads();  // the half's four weight tiles of this step are in LDS
 #pragma unroll
@@ -113,7 +117,7 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
                     const FragB xa{__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xs[wave][r16][32 * i + 8 * grp]))};
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const u32x4 w = *reinterpret_cast<const u32x4 *>(&wsh[buf][kh][u][r16][32 * i + 8 * grp]);
+                        const u32x4 w = *reinterpret_cast<const u32x4 *>(&stg.w[buf][kh][u][r16][32 * i + 8 * grp]);
                         acc[u] = mfma(xa, FragB{__builtin_bit_cast(bf16x8, wvalid[u] ? w : u32x4{0u, 0u, 0u, 0u})}, acc[u]);
                     }
                 }
@@ -202,8 +206,7 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
         za[kb] = frag_bits(*reinterpret_cast<const uint2 *>(p), *reinterpret_cast<const uint2 *>(p + 16));
     }
     const int ncols = a.H * a.d, nt = ncols / 16, ct0 = kh * (nt / 2), ct1 = kh ? nt : nt / 2;
-#pragma unroll 4
-    for (int ct = ct0; ct < ct1; ++ct) {
+    auto tile = [&](int ct) __attribute__((always_inline)) {  // z W_up^T + b of column tile ct
         const int c = 16 * ct + r16;
         const uint16_t *wr = a.w_up + (long)c * a.r + 4 * grp;
         f32x4 acc = zero4();
@@ -215,9 +218,37 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
         }
         const float bc = a.b[c];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const long tok = tok0 + 16 * tt + 4 * grp + e;
-            if (tok < a.Ntok) a.g[tok * ncols + c] = gate_log_alpha(acc[e] + bc);
+        for (int e = 0; e < 4; ++e) acc[e] += bc;
+        return acc;
+    };
+    if ((nt & 15) == 0) {
+        // Eight column tiles at a time go through the wave's LDS tile, and each token row then
+        // leaves as 512 contiguous bytes (two rows per store instruction); stored straight from
+        // the MFMA layout, every store wrote 64-byte pieces of four rows.
+        for (int cg8 = ct0; cg8 < ct1; cg8 += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const f32x4 acc = tile(cg8 + u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) stg.g[wave][4 * grp + e][16 * u + r16] = gate_log_alpha(acc[e]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int rr = 2 * j + (lane >> 5);
+                const long tok = tok0 + 16 * tt + rr;
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&stg.g[wave][rr][4 * (lane & 31)]);
+                if (tok < a.Ntok) *reinterpret_cast<f32x4 *>(a.g + tok * ncols + 16 * cg8 + 4 * (lane & 31)) = v;
+            }
+        }
+    } else {
+#pragma unroll 4
+        for (int ct = ct0; ct < ct1; ++ct) {
+            const f32x4 acc = tile(ct);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const long tok = tok0 + 16 * tt + 4 * grp + e;
+                if (tok < a.Ntok) a.g[tok * ncols + 16 * ct + r16] = gate_log_alpha(acc[e]);
+            }
         }
     }
 }
