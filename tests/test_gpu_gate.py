@@ -143,3 +143,25 @@ def test_gate_largest_rank_and_heads():
           f"g err {e_g:.2e} ({same.mean():.3f} identical z)")
     assert floored_rel(host(z_g), z_ref) <= 4e-3 and rel_inf(host(beta_g), beta_ref) <= 1e-5
     assert same.mean() >= 0.95 and e_g <= 1e-5
+
+
+def test_gate_prologue_prefill_width():
+    """The gate prologue at the width the benchmark uses (2048: the whole-line load path), 16 heads of
+    128 channels, rank 32, with a ragged last workgroup (16,421 tokens); every token checked."""
+    Ntok, Dm, H, d, r = 16384 + 37, 2048, 16, 128, 32
+    w_down, w_beta, w_up, b = ki.gate_weights(Dm, H, d, r, 93260)
+    x = ki.gate_hidden(Ntok, Dm, 93260)
+    z_g, beta_g, g_g = kda.gate(*upload_gate(x, w_down, w_beta, w_up, b), want_g=True)
+    torch.cuda.synchronize()
+    z_g, beta_g, g_g = host(z_g), host(beta_g), host(g_g)
+    z_ref, beta_ref, _ = oracle.gate(x, w_down, w_beta, w_up, b, H, d)
+    z_st = ki.bf16_round(z_ref.astype(np.float32)).astype(np.float64)
+    same = np.all(z_g == z_st, axis=1)
+    g_ref = oracle.gate_g(z_st, w_up, b, H, d)
+    e_z, e_b = floored_rel(z_g, z_ref), rel_inf(beta_g, beta_ref)
+    e_g = rel_inf(g_g[same], g_ref[same])
+    e_g_rest = floored_rel(g_g[~same], g_ref[~same]) if (~same).any() else 0.0
+    print(f"gate Ntok={Ntok} Dm={Dm}: z err {e_z:.2e}, beta err {e_b:.2e}, g err {e_g:.2e} "
+          f"({same.mean():.4f} identical z), other g err {e_g_rest:.2e}")
+    assert e_z <= 4e-3 and e_b <= 1e-5
+    assert same.mean() >= 0.95 and e_g <= 1e-5 and e_g_rest <= 5e-3
