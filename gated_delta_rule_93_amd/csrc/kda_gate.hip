@@ -8,9 +8,12 @@
 // One 512-thread workgroup per 64 tokens.  The down projection and the beta projection are one
 // skinny bf16 MFMA product over the model width (x rows as A fragments, the stacked weight rows
 // [W_down; w_beta] as B fragments), four column tiles at a time, the width split over two waves
-// per 16-token row tile.  z is rounded to bf16 once; the optional log(alpha) is formed from those
-// rounded values by the same MFMA and the same nonlinearity as the fused chunk-local kernel, so
-// the two paths agree bit for bit.
+// per 16-token row tile.  When the width is a multiple of 256 the operands reach the MFMAs through
+// LDS: x rows and weight rows are loaded as whole 128-byte lines, and the weight rows of a step
+// once per workgroup for its four row-tile waves.  z is rounded to bf16 once; the optional
+// log(alpha) is formed from those rounded values by the same MFMA and the same nonlinearity as
+// the fused chunk-local kernel, so the two paths agree bit for bit, and leaves through LDS as
+// 512-byte row segments.
 #include <utility>
 
 #include "kda_common.h"
@@ -34,8 +37,9 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + fast_e
 }  // namespace
 
 // Waves (tt, kh): row tile tt = w & 3 (16 tokens), half kh = w >> 2 of the model width for the
-// projections and of the log-alpha columns.  The width loop issues the loads of four k blocks
-// before their MFMAs, so each wave has 20 loads in flight.
+// projections and of the log-alpha columns.  The width loop works in steps of four k blocks; on
+// the direct path a wave issues a step's 20 loads before its MFMAs, on the whole-line path the
+// next step's 8 loads are in flight while the current step is formed from LDS.
 __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
     __shared__ uint16_t zs[kGateTokens][128 + 8];  // the block's rounded z rows (for log(alpha))
     __shared__ f32x4 red[4][4][64];                // upper-half partial sums of four column tiles
@@ -62,8 +66,10 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
     // Whole-line path (the width a multiple of 256, so both halves have the same whole steps): load j
     // of a wave covers rows 8 (j >> 1) + (l >> 3) and bytes 128 (j & 1) + 16 (l & 7) of each row's
     // 256-byte step, so every request is a whole 128-byte line; the operands are then read from LDS
-    // in the fragment layout.  Loaded this way (the other path puts 16 rows x 64 bytes in one load),
-    // the kernel ran 35 -> 30 us on x alone.
+    // in the fragment layout.  Loaded directly in the fragment layout, every load holds 16 rows x
+    // 64 bytes (each line fetched as two halves) and the four row-tile waves each fetch the same
+    // weight rows; the L1 then bounded the kernel (35 us on 16384 tokens of width 2048, 16 us
+    // this way).
     const bool lines = (nkb & 7) == 0;  // uniform over the workgroup
     const long lrow0 = tok0 + 16 * tt + (lane >> 3), lrow1 = lrow0 + 8;
     const uint16_t *xl[2] = {a.x + (lrow0 < a.Ntok ? lrow0 : a.Ntok - 1) * (long)a.Dm + 8 * (lane & 7),
