@@ -49,7 +49,14 @@ METRIC = "KDA prefill tokens/s + MFMA %; decode-step state GB/s + % HBM peak"
 # form (triangle-aware): 140.5 KFLOP.
 PREFILL_IN_BYTES = 3 * 256 + 512 + 4
 PREFILL_OUT_BYTES = 256
+PREFILL_BYTES = PREFILL_IN_BYTES + PREFILL_OUT_BYTES   # 1,540 B per token-head
 PREFILL_FLOP = 140.5e3
+# kernel names as rocprofv3 reports them
+K_LOCAL = "kda::chunk_local_kernel<true, 128, false>"
+K_SCAN_2T = "kda::chunk_scan_kernel<true, 128, 2, 2, false>"   # two column tiles per workgroup
+K_SCAN_1T = "kda::chunk_scan_kernel<true, 128, 1, 4, false>"   # one tile, four waves (few chains)
+K_DECODE = "kda::decode_step_kernel<unsigned short, 128, 128>"
+K_PREP = "kda::prep_kernel<unsigned short, 128, 4>"
 
 
 def log(msg):
@@ -495,41 +502,107 @@ def bench_varlen_layer(torch, kda, dev, reps=5):
         assert L.kda_fwd(kda.KDA_BF16, 1, T, H, d, d, p(cu_d), N, p(q), p(k), p(v), p(g), p(beta), 1.0, p(S0),
                          p(S), p(o), p(ws), nws, st) == 0
 
+    def local():
+        assert L.kda_fwd_chunk_local(kda.KDA_BF16, 1, T, H, d, d, p(cu_d), N, p(q), p(k), p(v), p(g), p(beta),
+                                     p(ws), nws, st) == 0
+
+    def scan():
+        assert L.kda_fwd_state_scan(kda.KDA_BF16, 1, T, H, d, d, p(cu_d), N, 1.0, p(S0), p(S), p(o), p(ws), nws,
+                                    st) == 0
+
     layer()
     torch.cuda.synchronize()
     ms = time_events(layer, reps, torch)
     ms_fwd = time_events(fwd, reps, torch)
+    ms_local = time_events(local, reps, torch)
+    ms_scan = time_events(scan, reps, torch)
     th = T * H
     return {"workload": f"{T} packed tokens (64 sequences, lengths U[512, 16384]), H=32, d=128: 2 prologue "
                         "launches (q, k) + chunked prefill with per-sequence S_0",
-            "ms_layer": ms, "ms_fwd": ms_fwd, "tokens_per_s": T / (ms / 1e3),
-            "fwd_algorithmic_GBs": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * th / ms_fwd / 1e6}
+            "ms_layer": ms, "ms_fwd": ms_fwd, "ms_chunk_local": ms_local, "ms_state_scan": ms_scan,
+            "tokens_per_s": T / (ms / 1e3), "token_heads": th,
+            "fwd_algorithmic_GBs": PREFILL_BYTES * th / ms_fwd / 1e6}
 
 
-def cpu_baseline(inp, min_seconds=10.0):
-    """The fp64 oracle on the prefill batch, repeated whole passes until ~10 s of wall time."""
-    import oracle
-    threads = oracle.default_threads()
-    R = oracle.Recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+def cpu_info():
+    """The host CPU as /proc/cpuinfo describes it (every identifying field, not only the model name)."""
+    info = {"os_cpu_count": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            first = f.read().split("\n\n")[0]
+        fields = dict(l.split(":", 1) for l in first.splitlines() if ":" in l)
+        fields = {k.strip(): v.strip() for k, v in fields.items()}
+        for k in ("vendor_id", "model name", "cpu family", "model", "stepping", "cpu MHz", "cache size"):
+            if k in fields:
+                info[k.replace(" ", "_")] = fields[k]
+    except OSError:
+        pass
+    try:
+        info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        pass
+    return info
+
+
+def _time_oracle(fn, min_seconds):
+    """Repeat fn() until min_seconds of wall time; returns (passes, seconds)."""
     passes = 0
     t0 = time.perf_counter()
     while True:
-        R.run(threads=threads)
+        fn()
         passes += 1
         wall = time.perf_counter() - t0
         if wall >= min_seconds or passes >= 200:
-            break
-    tokens = inp.B * inp.T * passes
-    model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), model)
-    except OSError:
-        pass
-    return {"value": tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "cpu_model": model, "os_cpu_count": os.cpu_count(),
+            return passes, wall
+
+
+def cpu_baseline(inp, min_seconds=10.0):
+    """The fp64 oracle (the plain token recurrence, one thread per (sequence, head) chain) timed on
+    this host on bounded samples of every workload; the headline figure is the prefill batch on all
+    threads.  Token throughput of the oracle is linear in the chains and tokens it runs (7 d_k d_v
+    fp64 flops per token-head), so a sample of chains stands for its whole workload: tokens/s of a
+    workload = token-heads/s / H."""
+    import oracle
+    import kda_inputs as ki
+    threads = oracle.default_threads()
+    R = oracle.Recurrence(inp.q, inp.k, inp.v, inp.g, inp.beta)
+    passes, wall = _time_oracle(lambda: R.run(threads=threads), min_seconds)
+    th_rate = inp.B * inp.T * inp.H * passes / wall
+    per = {}
+
+    def sample(name, q, k, v, g, beta, S0, H_workload, desc, nthreads, budget=1.5):
+        Rs = oracle.Recurrence(q, k, v, g, beta, 1.0, S0)
+        chains = [(n, h) for n in range(Rs.N) for h in range(Rs.H)]
+        n_, w_ = _time_oracle(lambda: Rs.run(chains, threads=nthreads), budget)
+        ths = sum(Rs.bounds(n)[2] for n, _ in chains) * n_ / w_
+        per[name] = {"token_heads_per_s": ths, "tokens_per_s": ths / H_workload, "threads": nthreads,
+                     "sample": desc, "passes": n_, "seconds": round(w_, 2)}
+
+    # small fp32 recurrence (B=1, H=2, T=256, d=64): the whole workload, one thread
+    s0 = ki.small_fp32()
+    sample("small_fp32_1thread", s0.q, s0.k, s0.v, s0.g, s0.beta, None, 2, "whole workload, 2 chains", 1, 1.0)
+    # prefill batch: 2 of its 64 chains on one thread (B=4 H=16 T=4096 shape, its distributions)
+    s1 = ki.make_dense(1, 4096, 2, 128, 128, "bf16", 93101)
+    sample("prefill_batch_1thread", s1.q, s1.k, s1.v, s1.g, s1.beta, None, 16,
+           "2 chains of 4096 tokens (d=128)", 1)
+    # long context: 2 chains of 32768 tokens (1/4 of T) on two threads
+    s2 = ki.make_dense(1, 32768, 2, 128, 128, "bf16", 93102, s0_std=0.02)
+    sample("long_context", s2.q, s2.k, s2.v, s2.g, s2.beta, s2.S0, 32,
+           "2 chains of 32768 tokens of the T=131072, H=32 shape", 2)
+    # decode pool: 100 steps of 8 (sequence, head) chains, one thread (a chain of 100 tokens each)
+    s3 = ki.make_dense(8, 100, 1, 128, 128, "bf16", 93103, s0_std=0.02)
+    sample("decode_pool_1thread", s3.q, s3.k, s3.v, s3.g, s3.beta, s3.S0, 32,
+           "8 of the 8192 chains over 100 steps; tokens/s = decode steps x sequences / s", 1)
+    # varlen layer: 2 heads of 2 of its sequences (lengths from the workload), two threads
+    lengths = ki.varlen_layer_lengths()[:2]
+    s4 = ki.make_varlen(lengths, 2, 128, 128, "bf16", 93104)
+    sample("varlen_layer", s4.q, s4.k, s4.v, s4.g, s4.beta, s4.S0, 32,
+           f"2 heads of sequences 0-1 (lengths {int(lengths[0])}, {int(lengths[1])})", 2)
+    return {"value": th_rate / inp.H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_info(),
             "sample": f"{passes} whole passes over the prefill batch (all {inp.B * inp.H} (sequence, head) "
-                      f"chains of {inp.T} tokens), fp64 token recurrence, {wall:.1f} s wall"}
+                      f"chains of {inp.T} tokens), fp64 token recurrence, {wall:.1f} s wall on {threads} threads",
+            "per_workload": per}
 
 
 def bench_copy(torch, dev, nbytes=1 << 28):
@@ -560,32 +633,157 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from profiles/traffic.json, if taken on the current source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _traffic_table():
     try:
-        with open(path) as fh:
+        with open(TRAFFIC_JSON) as fh:
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
-    k = t.get("kernels", {}).get(kernel)
+    return t if t.get("source_hash") == kernel_source_hash() else None
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` in the leg `workload` from profiles/traffic.json, if the
+    counters were taken on the current kernel source (None otherwise)."""
+    t = _traffic_table()
+    k = None if t is None else t.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
 
 
-def measured_mfma(kernel):
-    """rocprofv3 MfmaUtil (%) and issued bf16 MFMA flops per launch of `kernel` from
-    profiles/traffic.json, if taken on the current source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    try:
-        with open(path) as fh:
-            t = json.load(fh)
-    except (OSError, ValueError):
-        return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
-    return t.get("mfma", {}).get(kernel)
+def measured_mfma(workload, kernel):
+    """rocprofv3 MfmaUtil (%) and issued bf16 MFMA flops per launch of `kernel` in leg `workload`."""
+    t = _traffic_table()
+    return None if t is None else t.get("workloads", {}).get(workload, {}).get("mfma", {}).get(kernel)
+
+
+# ----------------------------------------------------------------------------- profile summaries
+# `python bench.py --summarize DIR` turns rocprofv3 csv output into profiles/traffic.json and the
+# text summaries under profiles/.  DIR/<leg>/ holds the output of three runs of one bench leg
+# (<leg> is a name of --only, e.g. prefill, long, varlen, decode, prep):
+#   rocprofv3 --kernel-trace --stats -f csv -d DIR/<leg>/trace -o trace -- python3 bench.py --only <leg>,copy
+#   rocprofv3 --pmc FETCH_SIZE       -f csv -d DIR/<leg>/fetch -o fetch -- python3 bench.py --only <leg>,copy
+#   rocprofv3 --pmc WRITE_SIZE       -f csv -d DIR/<leg>/write -o write -- python3 bench.py --only <leg>,copy
+# and optionally DIR/<leg>/mfma (--pmc MfmaUtil MfmaFlopsBF16).  The copy leg runs a 256 MiB
+# device copy in the same process: its FETCH_SIZE / WRITE_SIZE (KiB) against the 268,435,456 bytes
+# it reads and writes give the scale factors applied to every kernel of the leg.
+def _short_kernel(name):
+    name = name.replace("void ", "")
+    m = re.match(r"(kda::[a-z_]+(?:<[^>]*>)?|__amd_rocclr_copyBuffer)", name)
+    return m.group(1) if m else name[:60]
+
+
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    return None
+
+
+def _counters(path):
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = _short_kernel(r["Kernel_Name"])
+            if name.startswith("kda::") or name == "__amd_rocclr_copyBuffer":
+                per[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize_profiles(top, cmd_prefix="rocprofv3"):
+    import csv
+    copy_name, nb = "__amd_rocclr_copyBuffer", 1 << 28
+    table = {"source_hash": kernel_source_hash(), "workloads": {}}
+    for leg in sorted(os.listdir(top)):
+        d = os.path.join(top, leg)
+        if not os.path.isdir(d):
+            continue
+        entry = {"kernels": {}, "mfma": {}, "kernel_avg_us": {}}
+        md = [f"# rocprofv3 summary: bench leg `{leg}`", "",
+              f"Commands (run from /tmp on one MI355X with TMPDIR=/tmp; `<repo>` is this repository):", "", "```",
+              f"{cmd_prefix} --kernel-trace --stats -f csv -d <out>/{leg}/trace -o trace -- python3 <repo>/bench.py --only {leg},copy",
+              f"{cmd_prefix} --pmc FETCH_SIZE -f csv -d <out>/{leg}/fetch -o fetch -- python3 <repo>/bench.py --only {leg},copy",
+              f"{cmd_prefix} --pmc WRITE_SIZE -f csv -d <out>/{leg}/write -o write -- python3 <repo>/bench.py --only {leg},copy",
+              f"python3 <repo>/bench.py --summarize <out>", "```", ""]
+        stats = _find_csv(os.path.join(d, "trace"), "kernel_stats.csv")
+        if stats:
+            md += ["Kernel durations (`kernel_stats.csv`; torch's input-generation kernels omitted):", "",
+                   "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+            with open(stats) as fh:
+                for r in csv.DictReader(fh):
+                    k = _short_kernel(r["Name"])
+                    if k.startswith("kda::") or k == copy_name:
+                        avg = float(r["AverageNs"]) / 1e3
+                        entry["kernel_avg_us"][k] = avg
+                        md.append(f"| `{k}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                                  f"{float(r['MaxNs']) / 1e3:.1f} |")
+            md.append("")
+        fpath, wpath = _find_csv(os.path.join(d, "fetch"), "counter_collection.csv"), \
+            _find_csv(os.path.join(d, "write"), "counter_collection.csv")
+        if fpath and wpath:
+            fe, wr = _counters(fpath), _counters(wpath)
+            fcal, wcal = max(fe[copy_name]["FETCH_SIZE"]), max(wr[copy_name]["WRITE_SIZE"])
+            fs, ws = nb / (fcal * 1024), nb / (wcal * 1024)
+            entry.update(fetch_scale=fs, write_scale=ws)
+            md += [f"HBM traffic per launch: FETCH_SIZE x {fs:.3f} + WRITE_SIZE x {ws:.3f} (the 256 MiB runtime copy of "
+                   f"the same run reads {fcal:.0f} KiB by FETCH_SIZE and writes {wcal:.0f} KiB by WRITE_SIZE).", "",
+                   "| kernel | launches | read (MB) | written (MB) | total (MB) |", "|---|---|---|---|---|"]
+            for k in sorted(set(fe) & set(wr)):
+                f, w = fe[k].get("FETCH_SIZE"), wr[k].get("WRITE_SIZE")
+                if not f or not w:
+                    continue
+                if k == copy_name:
+                    f = [x for x in f if x > 0.99 * fcal]
+                    w = [x for x in w if x > 0.99 * wcal]
+                rd, wt = sum(f) / len(f) * 1024 * fs, sum(w) / len(w) * 1024 * ws
+                entry["kernels"][k] = {"bytes_read": rd, "bytes_written": wt, "bytes_per_launch": rd + wt,
+                                       "launches": len(f)}
+                md.append(f"| `{k}` | {len(f)} | {rd / 1e6:.1f} | {wt / 1e6:.1f} | {(rd + wt) / 1e6:.1f} |")
+            md.append("")
+        mpath = _find_csv(os.path.join(d, "mfma"), "counter_collection.csv")
+        if mpath:
+            mf = _counters(mpath)
+            md += ["MFMA counters (MfmaUtil %, issued bf16 MFMA flops per launch):", "",
+                   "| kernel | launches | MfmaUtil (%) | MfmaFlopsBF16 (GFLOP) |", "|---|---|---|---|"]
+            for k, c in sorted(mf.items()):
+                u, fl = c.get("MfmaUtil"), c.get("MfmaFlopsBF16")
+                if u and fl:
+                    entry["mfma"][k] = {"util_pct": sum(u) / len(u), "bf16_flops_issued": sum(fl) / len(fl)}
+                    md.append(f"| `{k}` | {len(u)} | {sum(u) / len(u):.1f} | {sum(fl) / len(fl) / 1e9:.2f} |")
+            md.append("")
+        table["workloads"][leg] = entry
+        with open(os.path.join(ROOT, "profiles", f"kda_{leg}_rocprof_summary.md"), "w") as fh:
+            fh.write("\n".join(md))
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(table, fh, indent=1)
+    return table
+
+
+def roofline_block(leg, th, ms_whole, kernels):
+    """Roofline figures of one prefill leg: the dominant kernel by the survey's algorithmic bytes
+    per token-head (1,540 B: q, k, v bf16, g fp32, beta, o bf16) over its own duration, the whole
+    prefill by the same bytes over the whole call, and each kernel's measured traffic."""
+    alg = PREFILL_BYTES * th
+    dom = max(kernels, key=lambda k: kernels[k][1])
+    dom_name, dom_ms = kernels[dom]
+    r = {"bound": "hbm", "kernel": dom_name, "algorithmic_bytes_per_launch": alg,
+         "achieved": alg / (dom_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = measured_traffic(leg, dom_name)
+    r["ms_per_launch"] = dom_ms
+    whole = {"bound": "hbm", "algorithmic_bytes": alg, "ms": ms_whole, "achieved": alg / (ms_whole / 1e3) / 1e9,
+             "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    whole["frac"] = whole["achieved"] / HBM_PEAK_GBS
+    tr = {k: measured_traffic(leg, name) for k, (name, _) in kernels.items()}
+    whole["traffic"] = None if any(v is None for v in tr.values()) else sum(tr.values())
+    per_kernel = {k: {"kernel": name, "ms": ms, "traffic": tr[k], "mfma": measured_mfma(leg, name)}
+                  for k, (name, ms) in kernels.items()}
+    return r, whole, per_kernel
 
 
 def main():
@@ -593,10 +791,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="write profiles/traffic.json and profiles/kda_<leg>_rocprof_summary.md from rocprofv3 "
+                         "csv output under DIR/<leg>/{trace,fetch,write,mfma} (no GPU needed)")
     ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,attnres,long,kcp,varlen,cpu",
                     help="comma list of prefill, decode, prep, scalar, gate, attnres, long, kcp, varlen, cpu, "
                          "copy")
     args = ap.parse_args()
+    if args.summarize:
+        t = summarize_profiles(args.summarize)
+        print(json.dumps({k: list(v["kernels"]) for k, v in t["workloads"].items()}))
+        return
     only = set(x.strip() for x in args.only.split(",") if x.strip())
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -607,7 +812,20 @@ def main():
     dev = torch.device("cuda:0")
     kda.lib()
 
-    if "prefill" not in only:  # profiling-only invocations
+    def long_block(lc):
+        th = 131072 * 32
+        r, whole, per = roofline_block("long", th, lc["ms"], {
+            "chunk_local": (K_LOCAL, lc["ms_chunk_local"]), "state_scan": (K_SCAN_1T, lc["ms_state_scan"])})
+        lc.update(roofline=r, roofline_whole=whole, kernels=per)
+        return lc
+
+    def varlen_block(vl):
+        r, whole, per = roofline_block("varlen", vl["token_heads"], vl["ms_fwd"], {
+            "chunk_local": (K_LOCAL, vl["ms_chunk_local"]), "state_scan": (K_SCAN_2T, vl["ms_state_scan"])})
+        vl.update(roofline=r, roofline_whole=whole, kernels=per)
+        return vl
+
+    if "prefill" not in only:  # single legs (profiling runs)
         out = {}
         if "decode" in only:
             out["decode"] = bench_decode(args, torch, kda, dev)
@@ -620,36 +838,25 @@ def main():
         if "attnres" in only:
             out["attnres"] = bench_attnres(torch, kda, dev)
         if "long" in only:
-            out["long_context"] = bench_long(torch, kda, dev)
+            out["long_context"] = long_block(bench_long(torch, kda, dev))
         if "kcp" in only:
             out["segment_maps"] = bench_kcp(torch, kda, dev)
         if "varlen" in only:
-            out["varlen_layer"] = bench_varlen_layer(torch, kda, dev)
+            out["varlen_layer"] = varlen_block(bench_varlen_layer(torch, kda, dev))
         if "copy" in only:
             out["copy"] = bench_copy(torch, dev)
+        if "cpu" in only:
+            import kda_inputs as ki
+            out["cpu_baseline"] = cpu_baseline(ki.prefill_batch())
         print(json.dumps(out), flush=True)
         return
     log("prefill ...")
     pf, inp = bench_prefill(args, torch, kda, dev)
     token_heads = pf["token_heads"]
     value = pf["tokens"] / (pf["ms_step"] / 1e3)
-    # dominant prefill kernel and its roofline (HBM-bound by arithmetic intensity)
     flops = PREFILL_FLOP * token_heads
-    if pf["ms_chunk_local"] >= pf["ms_state_scan"]:
-        # chunk-local kernel: streams the inputs; HBM-bound by arithmetic intensity
-        dom, dom_ms = "chunk_local_kernel", pf["ms_chunk_local"]
-        roof = {"bound": "hbm", "kernel": dom, "algorithmic_bytes_per_launch": PREFILL_IN_BYTES * token_heads,
-                "achieved": PREFILL_IN_BYTES * token_heads / (dom_ms / 1e3) / 1e9, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    else:
-        # state scan: its algorithmic work is the inter-chunk contractions (6 d^2 + (C+1) d per token-head)
-        dom, dom_ms = "chunk_scan_kernel", pf["ms_state_scan"]
-        scan_flop = (6 * 128 * 128 + 65 * 128) * token_heads
-        roof = {"bound": "mfma", "kernel": dom, "algorithmic_flop_per_launch": scan_flop,
-                "achieved": scan_flop / (dom_ms / 1e3) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom)
-    roof["ms_per_launch"] = dom_ms
+    roof, whole, per = roofline_block("prefill", token_heads, pf["ms_step"], {
+        "chunk_local": (K_LOCAL, pf["ms_chunk_local"]), "state_scan": (K_SCAN_2T, pf["ms_state_scan"])})
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": pf["ms_step"], "higher_is_better": True, "scaling": "weak",
@@ -658,13 +865,13 @@ def main():
                                "fp32 log-decay/beta/state", "global_batch": 4, "seq_len": 4096, "heads": 16,
                    "head_dim": 128, "parallelism": "single GPU"},
         "roofline": roof,
+        "roofline_whole_prefill": whole,
         "prefill": {"ms_fwd": pf["ms_fwd_events"], "ms_chunk_local": pf["ms_chunk_local"],
-                    "ms_state_scan": pf["ms_state_scan"],
-                    "algorithmic_GBs": (PREFILL_IN_BYTES + PREFILL_OUT_BYTES) * token_heads / pf["ms_fwd_events"] / 1e6,
+                    "ms_state_scan": pf["ms_state_scan"], "kernels": per,
+                    "algorithmic_GBs": PREFILL_BYTES * token_heads / pf["ms_fwd_events"] / 1e6,
                     "algorithmic_TFLOPs": flops / pf["ms_fwd_events"] / 1e9,
                     "mfma_frac_of_bf16_peak": flops / pf["ms_fwd_events"] / 1e9 / BF16_PEAK_TFLOPS,
                     "workspace_bytes_per_chunk_head": pf["ws_bytes_per_chunk_head"],
-                    "rocprof_mfma": {k: measured_mfma(k) for k in ("chunk_local_kernel", "chunk_scan_kernel")},
                     "untimed_settle_steps": pf["settle_steps"]},
     }
     if "decode" in only:
@@ -672,10 +879,10 @@ def main():
         dc = bench_decode(args, torch, kda, dev)
         out["decode"] = {"workload": "256 sequences x 32 heads, d=128, fp32 state, bf16 tokens, 100 steps",
                          "ms_per_step": dc["ms_step"], "state_GBs": dc["state_gbs"], "total_GBs": dc["total_gbs"],
-                         "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": dc["total_gbs"],
+                         "roofline": {"bound": "hbm", "kernel": K_DECODE, "achieved": dc["total_gbs"],
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": dc["total_gbs"] / HBM_PEAK_GBS,
-                                      "traffic": measured_traffic("decode_step_kernel"),
+                                      "traffic": measured_traffic("decode", K_DECODE),
                                       "algorithmic_bytes_per_launch": dc["state_bytes"] + dc["io_bytes"]}}
         cp = bench_copy(torch, dev)
         out["decode"]["copy_same_run"] = {"what": "runtime device copy of 256 MiB (read + write)",
@@ -685,10 +892,10 @@ def main():
         pr = bench_prep(args, torch, kda, dev)
         out["prep"] = {"workload": f"{pr['tokens']} packed tokens (64 sequences), H=32, d=128, width 4, bf16",
                        "ms": pr["ms"], "GBs": pr["gbs"], "frac": pr["gbs"] / HBM_PEAK_GBS,
-                       "roofline": {"bound": "hbm", "kernel": "prep_kernel", "achieved": pr["gbs"], "peak": HBM_PEAK_GBS,
+                       "roofline": {"bound": "hbm", "kernel": K_PREP, "achieved": pr["gbs"], "peak": HBM_PEAK_GBS,
                                     "unit": "GB/s", "frac": pr["gbs"] / HBM_PEAK_GBS,
                                     "algorithmic_bytes_per_launch": pr["bytes"],
-                                    "traffic": measured_traffic("prep_kernel")}}
+                                    "traffic": measured_traffic("prep", K_PREP)}}
     if "scalar" in only:
         log("scalar gate ...")
         out["scalar_gate"] = bench_scalar_gate(torch, kda, dev)
@@ -700,13 +907,13 @@ def main():
         out["attnres"] = bench_attnres(torch, kda, dev)
     if "long" in only:
         log("long context ...")
-        out["long_context"] = bench_long(torch, kda, dev)
+        out["long_context"] = long_block(bench_long(torch, kda, dev))
     if "kcp" in only:
         log("segment maps ...")
         out["segment_maps"] = bench_kcp(torch, kda, dev)
     if "varlen" in only:
         log("varlen layer ...")
-        out["varlen_layer"] = bench_varlen_layer(torch, kda, dev)
+        out["varlen_layer"] = varlen_block(bench_varlen_layer(torch, kda, dev))
     if "copy" in only:
         out["copy"] = bench_copy(torch, dev)
     if "cpu" in only:

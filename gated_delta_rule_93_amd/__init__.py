@@ -55,6 +55,8 @@ def lib():
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
         L.kda_fwd_workspace_bytes.restype = S
+        L.kda_fwd_workspace_min_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
+        L.kda_fwd_workspace_min_bytes.restype = S
         L.kda_fwd.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, F, P, P, P, P, S, P]
         L.kda_fwd.restype = I
         L.kda_fwd_scalar_gate.argtypes = [I, I, I, I, I, I, P, I, P, P, P, P, P, F, P, P, P, P, S, P]
@@ -140,7 +142,16 @@ def _stream(stream) -> int:
 
 
 def fwd_workspace_bytes(io: int, B: int, T: int, H: int, dk: int, dv: int, N: int, varlen: bool) -> int:
+    """Workspace for the prefill in one pass (kda_fwd_workspace_bytes)."""
     return int(lib().kda_fwd_workspace_bytes(io, B, T, H, dk, dv, N, 1 if varlen else 0))
+
+
+def fwd_workspace_min_bytes(io: int, B: int, T: int, H: int, dk: int, dv: int, N: int, varlen: bool,
+                            have_final_state: bool) -> int:
+    """Smallest workspace the prefill accepts; less than fwd_workspace_bytes runs it in windows
+    (kda_fwd_workspace_min_bytes)."""
+    return int(lib().kda_fwd_workspace_min_bytes(io, B, T, H, dk, dv, N, 1 if varlen else 0,
+                                                 1 if have_final_state else 0))
 
 
 def fwd(q, k, v, g, beta, scale: float = 1.0, initial_state=None, cu_seqlens=None,

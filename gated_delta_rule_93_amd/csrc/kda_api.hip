@@ -38,6 +38,14 @@ size_t kda_fwd_workspace_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int
     return (size_t)slots * (size_t)H * kda::fwd_bytes_per_chunk_head(io == KDA_BF16, d_k);
 }
 
+size_t kda_fwd_workspace_min_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, int N, int varlen,
+                                   int have_final_state) {
+    if (!valid_dtype(io) || B < 0 || T < 0 || H < 0 || N < 0) return 0;
+    if (d_k != d_v || !supported_d(d_k)) return 0;
+    if (varlen && B != 1) return 0;
+    return kda::fwd_min_workspace(io == KDA_BF16, d_k, B, T, H, N, varlen != 0, have_final_state != 0);
+}
+
 size_t kda_attnres_inter_workspace_bytes(int n, int L, int T) {
     if (n < 1 || n > kda::kAttnResMaxBlocks || L < 1 || L > kda::kAttnResMaxLayers || T < 0) return 0;
     return (size_t)n * (size_t)T * (16 + 1) * sizeof(float);
@@ -59,7 +67,7 @@ kda_status_t check_fwd(int part, kda_dtype_t io, int B, int T, int H, int d_k, i
         return KDA_ERR_INVALID_ARGUMENT;
     if (cu_seqlens) {
         if (B != 1) return KDA_ERR_INVALID_ARGUMENT;
-        if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned4(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;  // read as int32 scalars
     } else if (N != B) {
         return KDA_ERR_INVALID_ARGUMENT;
     }
@@ -76,7 +84,11 @@ kda_status_t check_fwd(int part, kda_dtype_t io, int B, int T, int H, int d_k, i
         }
     }
     if ((part & kScan) && ((s0 && !aligned16(s0)) || (sN && !aligned16(sN)))) return KDA_ERR_INVALID_ARGUMENT;
-    const size_t need = kda_fwd_workspace_bytes(io, B, T, H, d_k, d_v, N, cu_seqlens != nullptr);
+    // the whole prefill runs in windows when the workspace does not hold every chunk's record;
+    // its two phases called on their own need the whole workspace
+    const size_t need = part == kBoth
+                            ? kda::fwd_min_workspace(io == KDA_BF16, d_k, B, T, H, N, cu_seqlens != nullptr, sN != nullptr)
+                            : kda_fwd_workspace_bytes(io, B, T, H, d_k, d_v, N, cu_seqlens != nullptr);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return KDA_ERR_WORKSPACE;
     return KDA_OK;
 }
@@ -122,7 +134,7 @@ kda_status_t kda_fwd(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, cons
     if (st != KDA_OK || (long)N * H == 0) return st;
     const kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, scale, initial_state,
                                     final_state, o, workspace);
-    return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return kda::launch_fwd(a, workspace_bytes, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_fwd_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,
@@ -135,7 +147,7 @@ kda_status_t kda_fwd_scalar_gate(kda_dtype_t io, int B, int T, int H, int d_k, i
     kda::FwdArgs a = fwd_args(io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, scale, initial_state,
                               final_state, o, workspace);
     a.scalar_gate = true;
-    return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return kda::launch_fwd(a, workspace_bytes, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
@@ -154,7 +166,7 @@ kda_status_t kda_fwd_lowrank_gate(kda_dtype_t io, int B, int T, int H, int d_k, 
     a.gate_w_up = static_cast<const uint16_t *>(w_up);
     a.gate_b = b_gate;
     a.gate_r = r;
-    return kda::launch_fwd(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
+    return kda::launch_fwd(a, workspace_bytes, stream) == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH;
 }
 
 kda_status_t kda_gate(kda_dtype_t io, int Ntok, int Dm, int H, int d_k, int r, const void *x, const void *w_down,
@@ -362,7 +374,7 @@ kda_status_t kda_prep(kda_dtype_t io, int B, int T, int H, int d, const int32_t 
     if (W < 1 || W > 8) return W < 1 ? KDA_ERR_INVALID_ARGUMENT : KDA_ERR_UNSUPPORTED;
     if (cu_seqlens) {
         if (B != 1 || N < 1) return KDA_ERR_INVALID_ARGUMENT;
-        if (!aligned16(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;
+        if (!aligned4(cu_seqlens)) return KDA_ERR_INVALID_ARGUMENT;  // read as int32 scalars
     }
     if (!supported_d(d)) return KDA_ERR_UNSUPPORTED;
     if ((long)B * T * H == 0) return KDA_OK;

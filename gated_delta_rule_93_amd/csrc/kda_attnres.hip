@@ -241,38 +241,37 @@ hipError_t launch_attnres(const AttnResArgs &a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     const dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
     switch (a.d / 512) {
-        case 1: hipLaunchKernelGGL(attnres_online_kernel<1>, grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL(attnres_online_kernel<2>, grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL(attnres_online_kernel<3>, grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL(attnres_online_kernel<4>, grid, block, 0, st, a); break;
-        case 5: hipLaunchKernelGGL(attnres_online_kernel<5>, grid, block, 0, st, a); break;
-        case 6: hipLaunchKernelGGL(attnres_online_kernel<6>, grid, block, 0, st, a); break;
-        case 7: hipLaunchKernelGGL(attnres_online_kernel<7>, grid, block, 0, st, a); break;
-        case 8: hipLaunchKernelGGL(attnres_online_kernel<8>, grid, block, 0, st, a); break;
+        case 1: return launch_kernel(attnres_online_kernel<1>, grid, block, st, a);
+        case 2: return launch_kernel(attnres_online_kernel<2>, grid, block, st, a);
+        case 3: return launch_kernel(attnres_online_kernel<3>, grid, block, st, a);
+        case 4: return launch_kernel(attnres_online_kernel<4>, grid, block, st, a);
+        case 5: return launch_kernel(attnres_online_kernel<5>, grid, block, st, a);
+        case 6: return launch_kernel(attnres_online_kernel<6>, grid, block, st, a);
+        case 7: return launch_kernel(attnres_online_kernel<7>, grid, block, st, a);
+        case 8: return launch_kernel(attnres_online_kernel<8>, grid, block, st, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int NB>
-static void launch_mix(const AttnMixArgs &m, hipStream_t st) {
-    hipLaunchKernelGGL(attnres_mix_kernel<NB>, dim3((unsigned)((m.T + 3) / 4)), dim3(256), 0, st, m);
+static hipError_t launch_mix(const AttnMixArgs &m, hipStream_t st) {
+    return launch_kernel(attnres_mix_kernel<NB>, dim3((unsigned)((m.T + 3) / 4)), dim3(256), st, m);
 }
 
+// The mix kernel instance for m.n blocks; hipErrorInvalidValue when m.n is out of range.
 template <int... NBs>
-static bool launch_mix_n(const AttnMixArgs &m, hipStream_t st, std::integer_sequence<int, NBs...>) {
-    bool done = false;
-    ((m.n == NBs + 1 ? (launch_mix<NBs + 1>(m, st), done = true) : false), ...);
-    return done;
+static hipError_t launch_mix_n(const AttnMixArgs &m, hipStream_t st, std::integer_sequence<int, NBs...>) {
+    hipError_t e = hipErrorInvalidValue;
+    ((void)(m.n == NBs + 1 && ((e = launch_mix<NBs + 1>(m, st)), true)), ...);
+    return e;
 }
 
 hipError_t launch_attnres_inter(const AttnScoreArgs &s, const AttnMixArgs &m, hipStream_t st) {
     if (s.T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(attnres_scores_kernel, dim3((unsigned)((s.T + 63) / 64), (unsigned)s.n), dim3(256), 0, st, s);
-    hipError_t e = hipGetLastError();
+    const hipError_t e =
+        launch_kernel(attnres_scores_kernel, dim3((unsigned)((s.T + 63) / 64), (unsigned)s.n), dim3(256), st, s);
     if (e != hipSuccess) return e;
-    if (!launch_mix_n(m, st, std::make_integer_sequence<int, kAttnResMaxBlocks>{})) return hipErrorInvalidValue;
-    return hipGetLastError();
+    return launch_mix_n(m, st, std::make_integer_sequence<int, kAttnResMaxBlocks>{});
 }
 
 }  // namespace kda

@@ -27,6 +27,7 @@
 // Precision (bf16 inputs).  The Gram operands, Tm, Aqk, S and Ud enter the MFMAs as hi + lo
 // bf16 pairs (about 16 significant bits); U stays fp32.  q, k, v are used as stored (exact).
 // The fp32 path uses fp32 MFMAs throughout.
+#include <algorithm>
 #include <atomic>
 #include <type_traits>
 
@@ -87,8 +88,11 @@ template <> struct Prec<false> {
 
 // ------------------------------------------------------------------ workspace layout
 // Per (chunk slot, head): W, Qh fragments [tt][kb]; Kh^T fragments [rt][kb2]; Aqk fragments
-// (6 lower ones); e^gamma [D] (padded to 1 KB); U as accumulator tiles [jt][tt][lane] f32x4.
-// Everything before U is read by every column tile of the chain; U tile jt by one.
+// (6 lower ones); e^gamma [D] (padded to 1 KB); U as accumulator tiles [jt][tt][lane] f32x4;
+// for bf16, the low half of the hi + lo split of Kh^T [rt][kb2] (its high half is the Kh^T
+// plane above).  Everything before U is read by every column tile of the chain and is staged in
+// LDS by the state scan; U tile jt is read by column tile jt, the Kh^T low plane by each wave
+// for its own state rows.
 template <bool BF16, int D> struct WsLayout {
     static constexpr int NT = 4;           // 16-token tiles per chunk
     static constexpr int NKB = D / 32;     // 32-channel k-blocks
@@ -101,9 +105,25 @@ template <bool BF16, int D> struct WsLayout {
     static constexpr size_t offA = offK + (size_t)nK * PP * 1024;
     static constexpr size_t offE = offA + (size_t)nA * SP * 1024;
     static constexpr size_t offU = offE + 1024;
-    static constexpr size_t bytes = offU + (size_t)NRT * NT * 1024;
+    static constexpr size_t offKl = offU + (size_t)NRT * NT * 1024;
+    static constexpr size_t bytes = offKl + (BF16 ? (size_t)nK * 1024 : 0);
     static_assert(D * 4 <= 1024, "e^gamma fits its 1 KB slot");
 };
+
+// Kh^T fragment f of a record: the plain operand in the Kh^T plane and, for bf16, the low half of
+// its hi + lo split in the low plane (the state update takes the split: Kh^T single-rounded to
+// bf16 puts a relative error of 2^-9 on every product, which the state carries).
+template <bool BF16, int D>
+__device__ __forceinline__ void st_kh(char *wsb, int f, int lane, const float *kh) {
+    using L = WsLayout<BF16, D>;
+    if constexpr (BF16) {
+        const Frag2 s = make_frag2(kh);
+        reinterpret_cast<bf16x8 *>(wsb + L::offK)[f * 64 + lane] = s.h;
+        reinterpret_cast<bf16x8 *>(wsb + L::offKl)[f * 64 + lane] = s.l;
+    } else {
+        Prec<false>::st_plain(wsb + L::offK, L::nK, f, lane, make_fragF(kh));
+    }
+}
 
 // lower Aqk fragment index of (token tile tt, token k-block kb2), kb2 <= tt / 2
 __device__ __forceinline__ int aidx(int tt, int kb2) { return tt < 2 ? tt : 2 + 2 * (tt - 2) + kb2; }
@@ -119,23 +139,26 @@ __device__ __forceinline__ void pair_ij(int p, int &I, int &J) {
 __device__ __forceinline__ int bridge_idx(int I, int J) { return (I - 1) * I / 2 + J; }
 
 // ------------------------------------------------------------------ chunk addressing
+// The prefill runs its chunks in windows (one window when the workspace holds every chunk's
+// record).  Dense batch: window w holds the chunks c in [w Wc, (w + 1) Wc) of every sequence,
+// sequence n's chunk c at record n Wc + (c - w Wc).  Packed batch: window w holds the chunks whose
+// first token t0 has floor(t0 / 64) in [w Wc, (w + 1) Wc); the chunk's slot
+// n + floor(cu[n] / 64) + c = n + floor(t0 / 64) lies in [w Wc, (w + 1) Wc + N), and its record is
+// slot - w Wc.  Slots are injective, so every chunk has one record and no prefix pass is needed.
+struct Window {
+    int w;      // window index
+    long Wc;    // chunk indices per window
+    long nrec;  // records of this window (chunk-local grid = nrec * H workgroups)
+};
+
 struct ChunkPos {
     bool valid;
     int n, c, Cc;
     long tok0;
 };
 // Largest n in [0, N) with n + cu[n] / 64 <= slot (strictly increasing in n).
-__device__ __forceinline__ ChunkPos locate_chunk(long slot, const int32_t *cu, int N, int T) {
+__device__ __forceinline__ ChunkPos locate_packed(long slot, const int32_t *cu, int N) {
     ChunkPos p;
-    if (!cu) {
-        const int ncs = (T + kChunk - 1) / kChunk;
-        p.n = (int)(slot / ncs);
-        p.c = (int)(slot % ncs);
-        p.tok0 = (long)p.n * T + (long)p.c * kChunk;
-        p.Cc = min(kChunk, T - p.c * kChunk);
-        p.valid = true;
-        return p;
-    }
     int lo = 0, hi = N - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -147,6 +170,34 @@ __device__ __forceinline__ ChunkPos locate_chunk(long slot, const int32_t *cu, i
     p.valid = p.c >= 0 && (long)p.c * kChunk < L;
     p.tok0 = s + (long)p.c * kChunk;
     p.Cc = p.valid ? (int)min((long)kChunk, L - (long)p.c * kChunk) : 0;
+    return p;
+}
+
+// (record, head, chunk) of chunk-local workgroup `id` in window `win`.  The grid runs in reverse
+// consumption order: the chunks the state scan reads first are written last, so they are the
+// most likely to still be in the memory-side cache.
+__device__ __forceinline__ ChunkPos local_chunk(long id, const int32_t *cu, int N, int T, int H, const Window &win,
+                                                long &rec, int &h) {
+    if (cu) {
+        rec = win.nrec - 1 - id / H;
+        h = (int)(id % H);
+        ChunkPos p = locate_packed((long)win.w * win.Wc + rec, cu, N);
+        const long f = p.tok0 / kChunk;  // window of the chunk
+        p.valid = p.valid && f >= (long)win.w * win.Wc && f < (long)(win.w + 1) * win.Wc;
+        return p;
+    }
+    const long ncs = ((long)T + kChunk - 1) / kChunk;
+    const long c0 = (long)win.w * win.Wc, ncw = min(win.Wc, ncs - c0);  // chunks of this window
+    const long per_c = (long)N * H;
+    const long cl = ncw - 1 - id / per_c, rem = id % per_c;
+    h = (int)(rem % H);
+    ChunkPos p;
+    p.n = (int)(rem / H);
+    p.c = (int)(c0 + cl);
+    rec = (long)p.n * win.Wc + cl;
+    p.tok0 = (long)p.n * T + (long)p.c * kChunk;
+    p.Cc = (int)min((long)kChunk, (long)T - (long)p.c * kChunk);
+    p.valid = true;
     return p;
 }
 
@@ -331,24 +382,6 @@ __device__ __forceinline__ void ut_and_outputs(SM &sm, const Raw4<typename SM::T
     }
 }
 
-// (chunk slot, head) of chunk-local workgroup `id`.  The 1-D grid runs in reverse consumption
-// order: the chunks the state scan reads first are written last, so they are the most likely
-// to still be in the memory-side cache.
-__device__ __forceinline__ void local_slot(long id, const int32_t *cu, int N, int T, int H, long nslots,
-                                           long &slot, int &h) {
-    if (cu) {
-        slot = nslots - 1 - id / H;
-        h = (int)(id % H);
-    } else {
-        const int ncs = (T + kChunk - 1) / kChunk;
-        const long per_c = (long)N * H;
-        const int c = ncs - 1 - (int)(id / per_c);
-        const long rem = id % per_c;
-        h = (int)(rem % H);
-        slot = (rem / H) * ncs + c;
-    }
-}
-
 // The low-rank gate as the chunk-local kernel receives it (see LR below).
 struct LowRankGate {
     const uint16_t *z;     // [tokens, r] bf16 bits
@@ -366,7 +399,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ k,
                    const typename ChunkSmem<BF16, D>::TIO *__restrict__ v,
                    const float *__restrict__ g, const float *__restrict__ beta,
-                   const int32_t *__restrict__ cu, int N, int T, int H, long nslots, char *__restrict__ ws,
+                   const int32_t *__restrict__ cu, int N, int T, int H, Window win, char *__restrict__ ws,
                    LowRankGate lr) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     using P = Prec<BF16>;
@@ -376,14 +409,13 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     constexpr int NKB = L::NKB, NRT = L::NRT;
     __shared__ ChunkSmem<BF16, D> sm;
 
-    long slot;
+    long rec;
     int h;
-    local_slot(blockIdx.x, cu, N, T, H, nslots, slot, h);
-    const ChunkPos pos = locate_chunk(slot, cu, N, T);
+    const ChunkPos pos = local_chunk(blockIdx.x, cu, N, T, H, win, rec, h);
     if (!pos.valid) return;  // uniform over the block
     const int Cc = pos.Cc;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
-    char *wsb = ws + ((size_t)slot * H + h) * L::bytes;
+    char *wsb = ws + ((size_t)rec * H + h) * L::bytes;
     const long rowstride = (long)H * D;  // elements between consecutive tokens
     const long base_in = (pos.tok0 * H + h) * (long)D;
 
@@ -492,7 +524,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     __syncthreads();
 
     // ---------------- phase 2: element-wise products, written as operand fragments
-    char *wsQ = wsb + L::offQ, *wsK = wsb + L::offK;
+    char *wsQ = wsb + L::offQ;
     float *wsE = reinterpret_cast<float *>(wsb + L::offE);
     if (tid < D) wsE[tid] = fast_exp2(sm.g.G[kChunk - 1][tid]);
     for (int e = tid; e < 6 * D; e += 256) {
@@ -534,7 +566,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
                     kh[s] = kv * fast_exp2(gam - gt);
                     xv[s] = kv * fast_exp2(gt);
                 }
-                P::st_plain(wsK, L::nK, rt * 2 + kb2, lane, P::plain(kh));
+                st_kh<BF16, D>(wsb, rt * 2 + kb2, lane, kh);
                 Xf[r2][kb2] = P::plain(xv);
             }
         }
@@ -708,7 +740,7 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
                           const typename ChunkSmemS<BF16, D>::TIO *__restrict__ k,
                           const typename ChunkSmemS<BF16, D>::TIO *__restrict__ v,
                           const float *__restrict__ g, const float *__restrict__ beta,
-                          const int32_t *__restrict__ cu, int N, int T, int H, long nslots, char *__restrict__ ws) {
+                          const int32_t *__restrict__ cu, int N, int T, int H, Window win, char *__restrict__ ws) {
     using SM = ChunkSmemS<BF16, D>;
     using TIO = typename SM::TIO;
     using P = Prec<BF16>;
@@ -718,14 +750,13 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
     constexpr int RPG = SM::RPG;
     __shared__ SM sm;
 
-    long slot;
+    long rec;
     int h;
-    local_slot(blockIdx.x, cu, N, T, H, nslots, slot, h);
-    const ChunkPos pos = locate_chunk(slot, cu, N, T);
+    const ChunkPos pos = local_chunk(blockIdx.x, cu, N, T, H, win, rec, h);
     if (!pos.valid) return;  // uniform over the block
     const int Cc = pos.Cc;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
-    char *wsb = ws + ((size_t)slot * H + h) * L::bytes;
+    char *wsb = ws + ((size_t)rec * H + h) * L::bytes;
     const long rowstride = (long)H * D;
     const long base_in = (pos.tok0 * H + h) * (long)D;
 
@@ -770,7 +801,7 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
     __syncthreads();
 
     // ---------------- phase 2: Qh = Q e^G, Kh^T = (K e^{gamma - G})^T, X^T = (K e^G)^T
-    char *wsQ = wsb + L::offQ, *wsK = wsb + L::offK;
+    char *wsQ = wsb + L::offQ;
     float *wsE = reinterpret_cast<float *>(wsb + L::offE);
     if (tid < D) wsE[tid] = sm.eG[kChunk - 1];  // e^gamma, the same for every channel
     Plain Xf[2][2];
@@ -799,7 +830,7 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
                     kh[s] = kvv * egm[s];
                     xv[s] = kvv * eg[s];
                 }
-                P::st_plain(wsK, L::nK, rt * 2 + kb2, lane, P::plain(kh));
+                st_kh<BF16, D>(wsb, rt * 2 + kb2, lane, kh);
                 Xf[r2][kb2] = P::plain(xv);
             }
         }
@@ -894,9 +925,9 @@ template <bool BF16, int D> constexpr bool map_needs_load(int i) {
 template <bool BF16, int D, int NCT, int NS, bool MAP = false>
 __global__ void __launch_bounds__((scan_threads<BF16, D, NCT, NS>()))
 chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
-                  const float *__restrict__ s0, float *__restrict__ sN,
+                  const float *s0, float *sN,  // may alias: each element is read before it is written
                   typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws,
-                  float *__restrict__ sA) {
+                  float *__restrict__ sA, Window win) {
     using TIO = typename ChunkSmem<BF16, D>::TIO;
     using P = Prec<BF16>;
     using L = WsLayout<BF16, D>;
@@ -946,17 +977,31 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         return NS == 4 ? (tt < pp ? tt : max(tt - 1, 0)) : (tt >> 1);
     };
 
-    long s_tok, L_n, slot0;
+    // this chain's chunks in window `win` (see Window): [c_lo, c_hi); the state enters from s0 in
+    // the window that holds the sequence's first chunk and from sN (the state the previous window
+    // left) otherwise.  From here on s_tok, L_n and chunk indices count from chunk c_lo.
+    long s_tok, L_n, rec0;
     if (cu) {
         s_tok = cu[n];
         L_n = (long)cu[n + 1] - s_tok;
-        slot0 = n + s_tok / kChunk;
+        rec0 = n + s_tok / kChunk - (long)win.w * win.Wc;
     } else {
         s_tok = (long)n * T;
         L_n = T;
-        slot0 = (long)n * ((T + kChunk - 1) / kChunk);
+        rec0 = (long)n * win.Wc - (long)win.w * win.Wc;
     }
-    const long nck = (L_n + kChunk - 1) / kChunk;
+    const long nck_seq = (L_n + kChunk - 1) / kChunk;
+    const long first = cu ? s_tok / kChunk : 0;  // window coordinate of chunk 0
+    const long c_lo = max(0L, (long)win.w * win.Wc - first);
+    const long c_hi = min(nck_seq, (long)(win.w + 1) * win.Wc - first);
+    // an empty sequence hands its initial state on in window 0 only
+    const bool active = c_lo < c_hi || (nck_seq == 0 && win.w == 0);
+    if (!active) return;  // uniform over the workgroup
+    const long nck = max(0L, c_hi - c_lo);
+    s_tok += c_lo * kChunk;
+    L_n -= c_lo * kChunk;
+    const long slot0 = rec0 + c_lo;
+    const float *sin = c_lo == 0 ? s0 : sN;
     const int HD = H * D;
     auto record = [&](long c) __attribute__((always_inline)) { return ws + ((size_t)(slot0 + c) * H + h) * L::bytes; };
     auto copy_one = [&](const char *src, char *dst, int i) __attribute__((always_inline)) {
@@ -1050,7 +1095,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             S[r][e] = MAP ? (amap && 16 * (part * RTH + r) + 4 * grp + e == col ? 1.f : 0.f)
-                          : s0 ? s0[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] : 0.f;
+                          : sin ? sin[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] : 0.f;
 
     if (nck > 0) {
         if (!kProd) stage_all(0);
@@ -1080,6 +1125,16 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
                 }
         }
         if (more) prefetch_u(c + 1, u_nx);
+        // low plane of this part's Kh^T rows (bf16): straight from the record, used after the
+        // exchange barrier
+        FragB kl[BF16 ? RTH : 1][2];
+        if constexpr (BF16) {
+            const bf16x8 *pk = reinterpret_cast<const bf16x8 *>(record(c) + L::offKl) + lane;
+#pragma unroll
+            for (int r = 0; r < RTH; ++r)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) kl[r][kb2].h = pk[((part * RTH + r) * 2 + kb2) * 64];
+        }
         // this part's contribution to W S and Qh S, one k-block at a time (the split of the next
         // block's state rows can then issue while the products of this one run); every tile still
         // sums its k-blocks in the same order
@@ -1167,13 +1222,19 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         for (int r = 0; r < RTH; ++r) Sn[r] = S[r] * e_cur[r];
 #pragma unroll
         for (int i = 0; i < (MAP ? 0 : NOT); ++i) oo[i] = mfma(af[i][0], Uop[0], oo[i]);
+        // Kh^T as the state update takes it: hi + lo for bf16, fp32 as stored otherwise
+        auto khop = [&](int r, int kb2) __attribute__((always_inline)) {
+            const Plain hi = kEarlyK ? kf[r][kb2] : ldK(r, kb2);
+            if constexpr (BF16) return Frag2{hi.h, kl[r][kb2].h};
+            else return hi;
+        };
 #pragma unroll
-        for (int r = 0; r < RTH; ++r) Sn[r] = mfma(kEarlyK ? kf[r][0] : ldK(r, 0), Uop[0], Sn[r]);
+        for (int r = 0; r < RTH; ++r) Sn[r] = mfma(khop(r, 0), Uop[0], Sn[r]);
 #pragma unroll
         for (int i = 0; i < (MAP ? 0 : NOT); ++i)
             if (own_tile(i) >= 2) oo[i] = mfma(af[i][1], Uop[1], oo[i]);
 #pragma unroll
-        for (int r = 0; r < RTH; ++r) S[r] = mfma(kEarlyK ? kf[r][1] : ldK(r, 1), Uop[1], Sn[r]);
+        for (int r = 0; r < RTH; ++r) S[r] = mfma(khop(r, 1), Uop[1], Sn[r]);
         if (kProd) {
             // rows of this chunk (the previous ones were read before the exchange barrier)
 #pragma unroll
@@ -1229,27 +1290,68 @@ long fwd_chunk_slots(int B, int T, int N, bool varlen) {
     return varlen ? (long)N + ncs : (long)B * ncs;
 }
 
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Records of a window of Wc chunk indices (see Window): dense N Wc, packed Wc + N.
+static long window_records(long Wc, int N, bool varlen) { return varlen ? Wc + N : (long)N * Wc; }
+
+bool plan_fwd_windows(bool bf16, int d, int B, int T, int H, int N, bool varlen, bool have_final_state,
+                      size_t ws_bytes, WindowPlan &p) {
+    const size_t rec = fwd_bytes_per_chunk_head(bf16, d);
+    const long ncs = ((long)T + kChunk - 1) / kChunk;
+    const size_t full = (size_t)fwd_chunk_slots(B, T, N, varlen) * (size_t)H * rec;
+    p = WindowPlan{ncs, 1, 0, false};
+    if (ws_bytes >= full || ncs <= 1 || H == 0) return ws_bytes >= full;
+    // the state travels between windows in final_state, else in the workspace after the records
+    const size_t carry = have_final_state ? 0 : align256((size_t)N * H * d * d * sizeof(float));
+    if (ws_bytes <= carry) return false;
+    const size_t per_chunk = (varlen ? 1 : (size_t)N) * (size_t)H * rec;  // bytes per chunk index
+    const size_t fixed = varlen ? (size_t)N * H * rec : 0;
+    if (ws_bytes - carry < fixed + per_chunk) return false;
+    const long Wc = std::min<long>(ncs, (long)((ws_bytes - carry - fixed) / per_chunk));
+    p.Wc = Wc;
+    p.nwin = (ncs + Wc - 1) / Wc;
+    p.carry = !have_final_state;
+    p.carry_off = align256((size_t)window_records(Wc, N, varlen) * H * rec);
+    return true;
+}
+
+size_t fwd_min_workspace(bool bf16, int d, int B, int T, int H, int N, bool varlen, bool have_final_state) {
+    const size_t rec = fwd_bytes_per_chunk_head(bf16, d);
+    const long ncs = ((long)T + kChunk - 1) / kChunk;
+    const size_t full = (size_t)fwd_chunk_slots(B, T, N, varlen) * (size_t)H * rec;
+    if (ncs <= 1 || H == 0) return full;
+    const size_t carry = have_final_state ? 0 : align256((size_t)N * H * d * d * sizeof(float));
+    return std::min<size_t>(full, align256((size_t)window_records(1, N, varlen) * H * rec) + carry);
+}
+
+// Window w of a plan with Wc chunk indices per window (the whole batch when Wc covers every chunk).
+static Window make_window(const FwdArgs &a, long Wc, int w) {
+    const bool varlen = a.cu_seqlens != nullptr;
+    const long ncs = ((long)a.T + kChunk - 1) / kChunk;
+    Window win;
+    win.w = w;
+    win.Wc = Wc;
+    if (varlen) win.nrec = std::min<long>(Wc + a.N, (long)a.N + ncs - (long)w * Wc);
+    else win.nrec = (long)a.N * std::min<long>(Wc, ncs - (long)w * Wc);
+    return win;
+}
+static Window full_window(const FwdArgs &a) { return make_window(a, ((long)a.T + kChunk - 1) / kChunk, 0); }
+
 template <bool BF16, int D, bool LR = false>
-static hipError_t launch_local_t(const FwdArgs &a, hipStream_t st) {
-    using TIO = typename ChunkSmem<BF16, D>::TIO;
-    const long slots = fwd_chunk_slots(a.B, a.T, a.N, a.cu_seqlens != nullptr);
-    if (slots <= 0 || a.H <= 0) return hipSuccess;
+static hipError_t launch_local_t(const FwdArgs &a, const Window &win, hipStream_t st) {
+    if (win.nrec <= 0 || a.H <= 0) return hipSuccess;
     const LowRankGate lr{a.gate_z, a.gate_w_up, a.gate_b, a.gate_r};
-    hipLaunchKernelGGL((chunk_local_kernel<BF16, D, LR>), dim3((unsigned)(slots * a.H)), dim3(256), 0, st,
-                       (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T,
-                       a.H, slots, static_cast<char *>(a.ws), lr);
-    return hipGetLastError();
+    return launch_kernel(chunk_local_kernel<BF16, D, LR>, dim3((unsigned)(win.nrec * a.H)), dim3(256), st, a.q,
+                         a.k, a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T, a.H, win, a.ws, lr);
 }
 
 template <bool BF16, int D, int NCT, int NS, bool MAP>
-static hipError_t launch_scan_nct(const FwdArgs &a, hipStream_t st, int nchains) {
-    using TIO = typename ChunkSmem<BF16, D>::TIO;
+static hipError_t launch_scan_nct(const FwdArgs &a, const Window &win, hipStream_t st, int nchains) {
     const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NCT) * (MAP ? 2 : 1);
-    hipLaunchKernelGGL((chunk_scan_kernel<BF16, D, NCT, NS, MAP>), dim3((unsigned)blocks),
-                       dim3(scan_threads<BF16, D, NCT, NS>()), 0, st,
-                       a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale, MAP ? nullptr : a.s0, a.sN, (TIO *)a.o,
-                       (const char *)a.ws, MAP ? a.map_A : nullptr);
-    return hipGetLastError();
+    return launch_kernel(chunk_scan_kernel<BF16, D, NCT, NS, MAP>, dim3((unsigned)blocks),
+                         dim3(scan_threads<BF16, D, NCT, NS>()), st, a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale,
+                         MAP ? nullptr : a.s0, a.sN, a.o, a.ws, MAP ? a.map_A : nullptr, win);
 }
 
 // Compute units of the current device, queried once per device (the value never changes).
@@ -1271,54 +1373,65 @@ static int device_cu_count() {
 // share one LDS copy of the chunk's operands), else one with the state split over more waves.
 // The segment map (MAP) has twice the column tiles: those of B and those of A.
 template <bool BF16, int D, bool MAP = false>
-static hipError_t launch_scan_t(const FwdArgs &a, hipStream_t st) {
+static hipError_t launch_scan_t(const FwdArgs &a, const Window &win, hipStream_t st) {
     const int nchains = a.N * a.H;
     if (nchains <= 0) return hipSuccess;
     const int cus = device_cu_count();
     const long tiles = (long)nchains * (D / 16) * (MAP ? 2 : 1);
-    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2, 2, MAP>(a, st, nchains);
+    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2, 2, MAP>(a, win, st, nchains);
     // too few tiles to give every CU a two-tile workgroup: one tile per workgroup, and at
     // d = 128 four waves per tile (a shorter serial chain per chunk)
-    if constexpr (D == 128) return launch_scan_nct<BF16, D, 1, 4, MAP>(a, st, nchains);
-    else return launch_scan_nct<BF16, D, 1, 2, MAP>(a, st, nchains);
+    if constexpr (D == 128) return launch_scan_nct<BF16, D, 1, 4, MAP>(a, win, st, nchains);
+    else return launch_scan_nct<BF16, D, 1, 2, MAP>(a, win, st, nchains);
 }
 
 template <bool BF16, int D>
-static hipError_t launch_local_scalar_t(const FwdArgs &a, hipStream_t st) {
-    using TIO = typename ChunkSmemS<BF16, D>::TIO;
-    const long slots = fwd_chunk_slots(a.B, a.T, a.N, a.cu_seqlens != nullptr);
-    if (slots <= 0 || a.H <= 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_local_scalar_kernel<BF16, D>), dim3((unsigned)(slots * a.H)), dim3(256), 0, st,
-                       (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T,
-                       a.H, slots, static_cast<char *>(a.ws));
-    return hipGetLastError();
+static hipError_t launch_local_scalar_t(const FwdArgs &a, const Window &win, hipStream_t st) {
+    if (win.nrec <= 0 || a.H <= 0) return hipSuccess;
+    return launch_kernel(chunk_local_scalar_kernel<BF16, D>, dim3((unsigned)(win.nrec * a.H)), dim3(256), st, a.q,
+                         a.k, a.v, a.g, a.beta, a.cu_seqlens, a.N, a.T, a.H, win, a.ws);
 }
 
-hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) {
+static hipError_t launch_local_win(const FwdArgs &a, const Window &win, hipStream_t st) {
     if (a.scalar_gate) {
-        if (a.bf16) return a.dk == 128 ? launch_local_scalar_t<true, 128>(a, st) : launch_local_scalar_t<true, 64>(a, st);
-        return a.dk == 128 ? launch_local_scalar_t<false, 128>(a, st) : launch_local_scalar_t<false, 64>(a, st);
+        if (a.bf16) return a.dk == 128 ? launch_local_scalar_t<true, 128>(a, win, st) : launch_local_scalar_t<true, 64>(a, win, st);
+        return a.dk == 128 ? launch_local_scalar_t<false, 128>(a, win, st) : launch_local_scalar_t<false, 64>(a, win, st);
     }
     if (a.gate_z) {  // low-rank gate: bf16 only (checked by the caller)
-        return a.dk == 128 ? launch_local_t<true, 128, true>(a, st) : launch_local_t<true, 64, true>(a, st);
+        return a.dk == 128 ? launch_local_t<true, 128, true>(a, win, st) : launch_local_t<true, 64, true>(a, win, st);
     }
-    if (a.bf16) return a.dk == 128 ? launch_local_t<true, 128>(a, st) : launch_local_t<true, 64>(a, st);
-    return a.dk == 128 ? launch_local_t<false, 128>(a, st) : launch_local_t<false, 64>(a, st);
+    if (a.bf16) return a.dk == 128 ? launch_local_t<true, 128>(a, win, st) : launch_local_t<true, 64>(a, win, st);
+    return a.dk == 128 ? launch_local_t<false, 128>(a, win, st) : launch_local_t<false, 64>(a, win, st);
 }
 
-hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st) {
-    if (a.bf16) return a.dk == 128 ? launch_scan_t<true, 128>(a, st) : launch_scan_t<true, 64>(a, st);
-    return a.dk == 128 ? launch_scan_t<false, 128>(a, st) : launch_scan_t<false, 64>(a, st);
+static hipError_t launch_scan_win(const FwdArgs &a, const Window &win, hipStream_t st) {
+    if (a.bf16) return a.dk == 128 ? launch_scan_t<true, 128>(a, win, st) : launch_scan_t<true, 64>(a, win, st);
+    return a.dk == 128 ? launch_scan_t<false, 128>(a, win, st) : launch_scan_t<false, 64>(a, win, st);
 }
+
+hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st) { return launch_local_win(a, full_window(a), st); }
+
+hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st) { return launch_scan_win(a, full_window(a), st); }
 
 hipError_t launch_fwd_segment_map(const FwdArgs &a, hipStream_t st) {
-    if (a.bf16) return a.dk == 128 ? launch_scan_t<true, 128, true>(a, st) : launch_scan_t<true, 64, true>(a, st);
-    return a.dk == 128 ? launch_scan_t<false, 128, true>(a, st) : launch_scan_t<false, 64, true>(a, st);
+    const Window win = full_window(a);
+    if (a.bf16) return a.dk == 128 ? launch_scan_t<true, 128, true>(a, win, st) : launch_scan_t<true, 64, true>(a, win, st);
+    return a.dk == 128 ? launch_scan_t<false, 128, true>(a, win, st) : launch_scan_t<false, 64, true>(a, win, st);
 }
 
-hipError_t launch_fwd(const FwdArgs &a, hipStream_t st) {
-    hipError_t e = launch_fwd_local(a, st);
-    return e != hipSuccess ? e : launch_fwd_scan(a, st);
+hipError_t launch_fwd(const FwdArgs &a, size_t ws_bytes, hipStream_t st) {
+    WindowPlan p;
+    if (!plan_fwd_windows(a.bf16, a.dk, a.B, a.T, a.H, a.N, a.cu_seqlens != nullptr, a.sN != nullptr, ws_bytes, p))
+        return hipErrorInvalidValue;  // the caller checks the workspace first
+    FwdArgs b = a;
+    if (p.nwin > 1 && p.carry) b.sN = reinterpret_cast<float *>(static_cast<char *>(a.ws) + p.carry_off);
+    for (int w = 0; w < (int)p.nwin; ++w) {
+        const Window win = make_window(b, p.Wc, w);
+        hipError_t e = launch_local_win(b, win, st);
+        if (e == hipSuccess) e = launch_scan_win(b, win, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace kda

@@ -61,9 +61,8 @@ hipError_t launch_state_combine(int count, int d, const float *A, const float *S
     if (count <= 0) return hipSuccess;
     const unsigned tiles = (unsigned)((d / kTile) * (d / kTile));
     const dim3 grid((unsigned)count * tiles);
-    if (d == 128) hipLaunchKernelGGL(state_combine_kernel<128>, grid, dim3(256), 0, st, A, S, B, out);
-    else hipLaunchKernelGGL(state_combine_kernel<64>, grid, dim3(256), 0, st, A, S, B, out);
-    return hipGetLastError();
+    if (d == 128) return launch_kernel(state_combine_kernel<128>, grid, dim3(256), st, A, S, B, out);
+    return launch_kernel(state_combine_kernel<64>, grid, dim3(256), st, A, S, B, out);
 }
 
 }  // namespace kda

@@ -104,10 +104,8 @@ decode_step_kernel(const TIO *__restrict__ q, const TIO *__restrict__ k, const T
 template <typename TIO, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t st) {
     const long heads = (long)a.N * a.H;
-    hipLaunchKernelGGL((decode_step_kernel<TIO, DK, DV>), dim3((unsigned)heads), dim3(decode_threads<DK, DV>()), 0, st,
-                       (const TIO *)a.q, (const TIO *)a.k, (const TIO *)a.v, a.g, a.beta, a.scale,
-                       a.state, (TIO *)a.o);
-    return hipGetLastError();
+    return launch_kernel(decode_step_kernel<TIO, DK, DV>, dim3((unsigned)heads), dim3(decode_threads<DK, DV>()), st,
+                         a.q, a.k, a.v, a.g, a.beta, a.scale, a.state, a.o);
 }
 
 template <typename TIO>

@@ -262,8 +262,7 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
 hipError_t launch_gate(const GateArgs &a, hipStream_t st) {
     if (a.Ntok <= 0) return hipSuccess;
     const unsigned blocks = (unsigned)((a.Ntok + kGateTokens - 1) / kGateTokens);
-    hipLaunchKernelGGL(gate_kernel, dim3(blocks), dim3(512), 0, st, a);
-    return hipGetLastError();
+    return launch_kernel(gate_kernel, dim3(blocks), dim3(512), st, a);
 }
 
 }  // namespace kda

@@ -5,7 +5,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace kda {
+
+// Launch `kern` on `st` and return the runtime's status for this launch itself (hipLaunchKernel
+// reports it directly; no sticky error left on the thread by an earlier, unrelated call is read
+// or cleared).  Each argument is converted to the kernel's parameter type.
+template <typename... P, size_t... I>
+inline hipError_t launch_kernel_impl(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t st,
+                                     std::tuple<P...> &vals, std::index_sequence<I...>) {
+    void *ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {static_cast<void *>(&std::get<I>(vals))...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kern), grid, block, ptrs, 0, st);
+}
+template <typename... P, typename... A>
+inline hipError_t launch_kernel(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t st, A &&...args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> vals{static_cast<P>(args)...};
+    return launch_kernel_impl(kern, grid, block, st, vals, std::index_sequence_for<P...>{});
+}
 
 struct DecodeArgs {
     bool bf16;
@@ -50,7 +69,20 @@ struct FwdArgs {
 // Bytes of workspace for one (chunk, head) and the number of chunk slots.
 size_t fwd_bytes_per_chunk_head(bool bf16, int d);
 long fwd_chunk_slots(int B, int T, int N, bool varlen);
-hipError_t launch_fwd(const FwdArgs &a, hipStream_t st);          // both phases
+// How kda_fwd splits the chunks into windows for a workspace of ws_bytes: Wc chunk indices per
+// window, nwin windows; with carry, the state travels between windows in the workspace at
+// carry_off (no final_state given).  False when the workspace is too small for one chunk per
+// window.  fwd_min_workspace is the smallest workspace plan_fwd_windows accepts.
+struct WindowPlan {
+    long Wc, nwin;
+    size_t carry_off;
+    bool carry;
+};
+bool plan_fwd_windows(bool bf16, int d, int B, int T, int H, int N, bool varlen, bool have_final_state,
+                      size_t ws_bytes, WindowPlan &p);
+size_t fwd_min_workspace(bool bf16, int d, int B, int T, int H, int N, bool varlen, bool have_final_state);
+// Both phases over the windows that a workspace of ws_bytes allows.
+hipError_t launch_fwd(const FwdArgs &a, size_t ws_bytes, hipStream_t st);
 hipError_t launch_fwd_local(const FwdArgs &a, hipStream_t st);    // chunk-local phase
 hipError_t launch_fwd_scan(const FwdArgs &a, hipStream_t st);     // state-scan phase
 // The affine map S_out = A S_in + B of every (sequence, head) chain, from the chunk-local records

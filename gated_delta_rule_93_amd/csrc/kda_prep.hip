@@ -195,15 +195,13 @@ static hipError_t launch_prep_d(const PrepArgs &a, hipStream_t st) {
     switch (a.W) {
 #define KDA_PREP_W(WW)                                                                                \
     case WW:                                                                                          \
-        hipLaunchKernelGGL((prep_kernel<TIO, D, WW>), grid, dim3(256), 0, st, x, a.w, y, a.cu_seqlens, \
-                           a.N, a.T, ntok, a.H);                                                      \
-        break;
+        return launch_kernel(prep_kernel<TIO, D, WW>, grid, dim3(256), st, x, a.w, y, a.cu_seqlens, a.N, a.T, \
+                             ntok, a.H);
         KDA_PREP_W(1) KDA_PREP_W(2) KDA_PREP_W(3) KDA_PREP_W(4)
         KDA_PREP_W(5) KDA_PREP_W(6) KDA_PREP_W(7) KDA_PREP_W(8)
 #undef KDA_PREP_W
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_prep(const PrepArgs &a, hipStream_t st) {

@@ -56,12 +56,28 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 const char *kda_status_string(kda_status_t status);
 
 /*
- * Workspace needed by kda_fwd for these sizes (bytes, a multiple of 256).
+ * Workspace for kda_fwd to run every chunk in one pass (bytes, a multiple of 256); the two phases
+ * kda_fwd_chunk_local / kda_fwd_state_scan and kda_fwd_segment_map always need this much.
+ * It is one record per (chunk, head): 95,232 bytes at d = 128 in bf16 (1,488 bytes per
+ * token-head), i.e. it grows with T * H (about 390 MB for 4 x 4096 tokens x 16 heads, 6.2 GB for
+ * 131,072 tokens x 32 heads).  A packed batch has N extra chunk slots (sequences need not start
+ * on a chunk boundary).
  * varlen != 0 means cu_seqlens will be passed; then B must be 1 and T is the packed
  * token count.  Returns 0 for unsupported or invalid sizes.
  */
 size_t kda_fwd_workspace_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
                                int N, int varlen);
+
+/*
+ * Smallest workspace kda_fwd, kda_fwd_scalar_gate and kda_fwd_lowrank_gate accept for these
+ * sizes (bytes).  Given less than kda_fwd_workspace_bytes, they run the chunks in windows: the
+ * chunk-local phase and the state scan of one window, then the next (see kda_fwd), so the
+ * workspace holds one window's records, plus the running state of every (sequence, head) when
+ * no final_state buffer carries it (have_final_state == 0).  The minimum is one chunk per window.
+ * Returns 0 for unsupported or invalid sizes.
+ */
+size_t kda_fwd_workspace_min_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                                   int N, int varlen, int have_final_state);
 
 /*
  * kda_fwd -- chunked prefill over a dense batch or a packed (varlen) batch.
@@ -84,7 +100,15 @@ size_t kda_fwd_workspace_bytes(kda_dtype_t io, int B, int T, int H, int d_k, int
  *   initial_state [N, H, d_k, d_v] fp32 or NULL (zero state)
  *   final_state   [N, H, d_k, d_v] fp32 or NULL (not written); may alias initial_state
  *   o             [B, T, H, d_v] io dtype, written for every token; must not alias inputs
- *   workspace     device buffer of at least kda_fwd_workspace_bytes(...) bytes
+ *   workspace     device buffer of at least kda_fwd_workspace_min_bytes(...) bytes (16-byte
+ *                 aligned), reused freely by the library during the call.  With
+ *                 kda_fwd_workspace_bytes(...) bytes or more every chunk runs in one pass;
+ *                 with less, in windows as large as the workspace allows: a dense batch takes
+ *                 chunks [w Wc, (w + 1) Wc) of every sequence in window w, a packed batch the
+ *                 chunks whose first token lies in [64 w Wc, 64 (w + 1) Wc).  Results are the
+ *                 same to rounding (the chunks and their arithmetic do not change; only when
+ *                 each is formed), and bitwise the same for any window size on one device.
+ *   Returns KDA_ERR_WORKSPACE when workspace is NULL or smaller than the minimum.
  */
 kda_status_t kda_fwd(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
                      const int32_t *cu_seqlens, int N,

@@ -52,8 +52,8 @@ def _store(x: np.ndarray, io: str) -> np.ndarray:
 
 
 def _softplus(x: np.ndarray) -> np.ndarray:
-    x = x.astype(np.float64)
-    return np.where(x > 30.0, x, np.log1p(np.exp(np.minimum(x, 30.0))))
+    """log(1 + e^x) in fp64 (numpy's overflow-free logaddexp)."""
+    return np.logaddexp(0.0, x.astype(np.float64))
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:
@@ -241,14 +241,37 @@ def small_fp32() -> KDAInputs:
     return make_dense(1, 256, 2, 64, 64, "f32", SEED_BASE + 0)
 
 
-def prefill_batch() -> KDAInputs:
-    """Chunked prefill: B=4, H=16, T=4096, d=128, bf16 q/k/v, S0 = 0."""
-    return make_dense(4, 4096, 16, 128, 128, "bf16", SEED_BASE + 1)
+def prefill_batch(g_shift: float = 2.0) -> KDAInputs:
+    """Chunked prefill: B=4, H=16, T=4096, d=128, bf16 q/k/v, S0 = 0.  g_shift = -5 draws the
+    weak-decay variant (alpha ~ 0.99)."""
+    return make_dense(4, 4096, 16, 128, 128, "bf16", SEED_BASE + 1, g_shift=g_shift)
 
 
-def long_context() -> KDAInputs:
-    """Long-context prefill: B=1, H=32, T=131072, d=128, bf16 q/k/v, S0 ~ N(0, 0.02)."""
-    return make_dense(1, 131072, 32, 128, 128, "bf16", SEED_BASE + 2, s0_std=0.02)
+LONG_CONTEXT = dict(B=1, T=131072, H=32, d=128, seed=SEED_BASE + 2)
+
+
+def long_context(g_shift: float = 2.0) -> KDAInputs:
+    """Long-context prefill: B=1, H=32, T=131072, d=128, bf16 q/k/v, S0 ~ N(0, 0.02).  g_shift = -5
+    draws the weak-decay variant (alpha ~ 0.99)."""
+    c = LONG_CONTEXT
+    return make_dense(c["B"], c["T"], c["H"], c["d"], c["d"], "bf16", c["seed"], s0_std=0.02, g_shift=g_shift)
+
+
+def dense_gate(B: int, T: int, H: int, dk: int, dv: int, seed: int, g_shift: float) -> np.ndarray:
+    """The g of make_dense(B, T, H, dk, dv, ., seed, g_shift=g_shift) alone, bitwise: the same
+    generator is advanced past the draws of q, k, v and x_beta (not processed), then x_alpha is
+    drawn and shifted."""
+    rng = np.random.default_rng(seed)
+    for shape in ((B, T, H, dk), (B, T, H, dk), (B, T, H, dv), (B, T, H)):
+        rng.standard_normal(shape, dtype=np.float32)
+    xa = rng.standard_normal((B, T, H, dk), dtype=np.float32)
+    return _map_f32(lambda a: -_softplus(a.astype(np.float64) + g_shift), xa)
+
+
+def long_context_gate(g_shift: float) -> np.ndarray:
+    """The g of long_context(g_shift) alone (bitwise)."""
+    c = LONG_CONTEXT
+    return dense_gate(c["B"], c["T"], c["H"], c["d"], c["d"], c["seed"], g_shift)
 
 
 DECODE_POOL = dict(N=256, H=32, d=128, steps=100, seed=SEED_BASE + 3)

@@ -150,11 +150,9 @@ class Recurrence:
             return n, 0, self.T
         return 0, int(self.cu[n]), int(self.cu[n + 1] - self.cu[n])
 
-    def run_chain(self, n: int, h: int, upto: Optional[int] = None):
-        """o [L', dv] and final state of chain (n, h), over the first `upto` tokens if given."""
+    def run_chain(self, n: int, h: int):
+        """o [L, dv] and final state of chain (n, h)."""
         b, s, L = self.bounds(n)
-        if upto is not None:
-            L = min(L, int(upto))
         H, dk, dv = self.H, self.dk, self.dv
         itm = 4
         base_tok = (b * self.T + s) * H + h
@@ -175,15 +173,14 @@ class Recurrence:
             raise MemoryError("oracle chain allocation failed")
         return o, S
 
-    def run(self, chains: Optional[Sequence[Tuple[int, int]]] = None, threads: Optional[int] = None,
-            upto: Optional[int] = None):
+    def run(self, chains: Optional[Sequence[Tuple[int, int]]] = None, threads: Optional[int] = None):
         """Run chains in parallel threads; returns {(n, h): (o, S)}."""
         if chains is None:
             chains = [(n, h) for n in range(self.N) for h in range(self.H)]
         chains = list(chains)
         threads = threads or default_threads()
         with ThreadPoolExecutor(max_workers=threads) as ex:
-            res = list(ex.map(lambda nh: self.run_chain(nh[0], nh[1], upto), chains))
+            res = list(ex.map(lambda nh: self.run_chain(nh[0], nh[1]), chains))
         return dict(zip(chains, res))
 
     def run_all(self, threads: Optional[int] = None):

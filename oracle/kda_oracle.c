@@ -13,9 +13,9 @@
  *     read-out   o_t = scale * S_t^T q_t          (the updated state is read)
  *   The per-channel decay acts on the key axis (page "Kimi K3 注意力三件套",
  *   KDA section: alpha_t in [0,1]^{d_k}; blog post ciyuanerhao post-114,
- *   chapter 4: alpha.unsqueeze(-1) * S on a [d_k, d_v] state).
+ *   chapter 4: the per-channel factor scales the rows of a d_k x d_v state).
  *   State orientation is K-major: S[i*dv + j] couples key channel i with value
- *   channel j, as in the blog's DeltaNet code (v_old = k @ S, S += k^T @ u).
+ *   channel j (the chapter 3 DeltaNet of that blog keeps its memory d_k x d_v).
  *
  * Inputs are the stored fp32 (or bf16-valued fp32) numbers, converted to double
  * exactly.  Nothing is clamped: NaN and Inf propagate.

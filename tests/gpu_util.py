@@ -1,10 +1,14 @@
 """Helpers for the GPU parity tests: device uploads and the error measures.
 
 Error measures (the fp64 oracle output is the reference r, never rounded):
-  fp32 path:  rel_inf(y, r)     = max|y - r| / max|r|                      (gate 1e-4)
-  bf16 path:  floored_rel(y, r) = max_i |y_i - r_i| / max(|r_i|, rms(r))   (gate 2e-2)
-The bf16 gate is a maximum relative error whose denominator is floored at the RMS of the
-reference, so elements far below the RMS are held to an absolute error of 2e-2 * RMS.
+  fp32 path:          rel_inf(y, r)     = max|y - r| / max|r|                      (gate 1e-4)
+  bf16 path, o:       floored_rel(y, r) = max_i |y_i - r_i| / max(|r_i|, rms(r))   (gate 2e-2)
+  bf16 path, states:  rms_rel(y, r)     = max|y - r| / rms(r)                      (gate 2e-2)
+The bf16 output gate is a maximum relative error whose denominator is floored at the RMS of the
+reference, so elements far below the RMS are held to an absolute error of 2e-2 * RMS: the
+output is stored in bf16 and heavy-tailed, so rounding the exact answer alone gives
+max|y - r| / rms(r) of ~0.04.  States are stored in fp32, so they take the normalised-by-RMS
+bound as it stands (err_state).
 """
 from __future__ import annotations
 
@@ -44,8 +48,20 @@ def floored_rel(y, r) -> float:
     return float(np.max(np.abs(y - r) / np.maximum(np.abs(r), max(rms, 1e-300))))
 
 
+def rms_rel(y, r) -> float:
+    y, r = np.asarray(y, np.float64), np.asarray(r, np.float64)
+    rms = float(np.sqrt(np.mean(r * r)))
+    return float(np.max(np.abs(y - r)) / max(rms, 1e-300))
+
+
 def err(y, r, io: str) -> float:
+    """Error of an io-dtype output (o, prologue y) against the fp64 reference."""
     return floored_rel(y, r) if io == "bf16" else rel_inf(y, r)
+
+
+def err_state(y, r, io: str) -> float:
+    """Error of an fp32 state (final state of a bf16 or fp32 run) against the fp64 reference."""
+    return rms_rel(y, r) if io == "bf16" else rel_inf(y, r)
 
 
 def tol(io: str) -> float:

@@ -11,8 +11,8 @@ Sources:
     d_k x d_v, o_t = q_t S_t), section 3 (decay then delta write);
   * page "Kimi K3 注意力三件套" (yeyulingfeng.com), KDA section: the factor
     (I - beta_t k_t k_t^T), the delta rule as one gradient-descent step, alpha over d_k;
-  * blog post ciyuanerhao post-114: chapter 3 (DeltaNet and Gated DeltaNet code),
-    chapter 4 (per-channel alpha multiplies the rows of S).
+  * blog post ciyuanerhao post-114: chapter 3 (DeltaNet writes the prediction error; Gated
+    DeltaNet adds one decay per token), chapter 4 (per-channel alpha multiplies the rows of S).
 """
 from __future__ import annotations
 
@@ -173,32 +173,35 @@ pin_high_precision.tol = 1e-14
 
 
 def pin_deltanet(chain_fn, seed=21, L=9, dk=4, dv=6):
-    """alpha == 1 reduces KDA to DeltaNet (blog post-114 ch. 3 DeltaNet code, row-vector form).
+    """alpha == 1 reduces KDA to DeltaNet (blog post-114, chapter 3: DeltaNet writes only the
+    prediction error; course page, section 3, with the decay factor equal to one).
 
-    v_old = k @ S; u = beta (v - v_old); S = S + k^T @ u; o = q @ S.
+    Written here in the course page's own orientation, a d_v x d_k memory M (M = S^T):
+    M_t = M_{t-1} + beta_t (v_t - M_{t-1} k_t) k_t^T and o_t = M_t q_t, with explicit
+    outer products; the oracle keeps the K-major transpose, so the two share no layout.
     """
     q, k, v, _, beta, S0 = _rand_case(seed, L, dk, dv)
-    S = S0.astype(np.float64)
+    M = S0.astype(np.float64).T.copy()           # d_v x d_k
     o_ref = np.zeros((L, dv))
     for t in range(L):
-        kr = k[t:t + 1].astype(np.float64)
-        v_old = kr @ S
-        u = float(beta[t]) * (v[t:t + 1].astype(np.float64) - v_old)
-        S = S + kr.T @ u
-        o_ref[t] = (q[t:t + 1].astype(np.float64) @ S)[0]
+        kt, vt, qt = (x[t].astype(np.float64) for x in (k, v, q))
+        err = vt - M.dot(kt)                      # prediction error of the memory for key k_t
+        M = M + float(beta[t]) * np.outer(err, kt)
+        o_ref[t] = M.dot(qt)
     o, Sn = chain_fn(q, k, v, np.zeros((L, dk), np.float32), beta, 1.0, S0)
-    return max(_rel(o, o_ref), _rel(Sn, S))
+    return max(_rel(o, o_ref), _rel(Sn, M.T))
 
 
 pin_deltanet.tol = 1e-12
 
 
 def pin_gated_deltanet_scalar(chain_fn, seed=31, L=9, dk=4, dv=5):
-    """All channels sharing one alpha_t gives Gated DeltaNet, decay-first order.
+    """All channels sharing one alpha_t gives Gated DeltaNet (blog post-114, chapter 3), with
+    the decay applied first as in the course page's section 3.
 
-    S = a_t S; v_old = k @ S; u = beta (v - v_old); S = S + k^T u; o = q @ S.
-    (Gated DeltaNet of blog post-114 ch. 3 with the decay placed first as in the course
-    page's section 3.)
+    Written as a transition plus an input, with the factor named in the KDA section of the page
+    "Kimi K3 注意力三件套": S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, formed with
+    an explicit d_k x d_k matrix (a scalar a_t commutes with the factor).
     """
     q, k, v, _, beta, S0 = _rand_case(seed, L, dk, dv)
     rng = np.random.default_rng(seed + 1)
@@ -206,12 +209,13 @@ def pin_gated_deltanet_scalar(chain_fn, seed=31, L=9, dk=4, dv=5):
     g = np.repeat(gs[:, None], dk, axis=1)
     S = S0.astype(np.float64)
     o_ref = np.zeros((L, dv))
+    eye = np.eye(dk)
     for t in range(L):
-        S = math.exp(float(gs[t])) * S
-        kr = k[t:t + 1].astype(np.float64)
-        u = float(beta[t]) * (v[t:t + 1].astype(np.float64) - kr @ S)
-        S = S + kr.T @ u
-        o_ref[t] = (q[t:t + 1].astype(np.float64) @ S)[0]
+        kt = k[t].astype(np.float64)
+        b = float(beta[t])
+        A = math.exp(float(gs[t])) * (eye - b * np.outer(kt, kt))
+        S = A.dot(S) + b * np.outer(kt, v[t].astype(np.float64))
+        o_ref[t] = S.T.dot(q[t].astype(np.float64))
     o, Sn = chain_fn(q, k, v, g, beta, 1.0, S0)
     return max(_rel(o, o_ref), _rel(Sn, S))
 

@@ -67,6 +67,8 @@ def fwd_call(**over):
     (dict(k=FAKE + 4), kda.KDA_ERR_INVALID_ARGUMENT),              # misaligned
     (dict(s0=FAKE + 8), kda.KDA_ERR_INVALID_ARGUMENT),
     (dict(cu=FAKE, B=2, N=2), kda.KDA_ERR_INVALID_ARGUMENT),       # varlen needs B = 1
+    (dict(cu=FAKE + 2), kda.KDA_ERR_INVALID_ARGUMENT),             # cu_seqlens not int32-aligned
+    (dict(cu=FAKE + 4, wsb=1024), kda.KDA_ERR_WORKSPACE),          # 4-byte aligned cu_seqlens passes
     (dict(dk=96, dv=96), kda.KDA_ERR_UNSUPPORTED),
     (dict(dk=128, dv=64), kda.KDA_ERR_UNSUPPORTED),
     (dict(ws=None), kda.KDA_ERR_WORKSPACE),
@@ -324,3 +326,26 @@ def test_chunk_local_gate_forms_reject():
     assert lr(io=kda.KDA_F32) == kda.KDA_ERR_UNSUPPORTED
     assert lr(z=None) == kda.KDA_ERR_INVALID_ARGUMENT
     assert lr(w_up=FAKE + 2) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_min_bytes():
+    """The windowed minimum: one chunk index of records (+ the carried states when no final_state
+    buffer carries them), never more than the one-pass workspace; sizes beyond 2^32 bytes stay exact."""
+    io = kda.KDA_BF16
+    rec = kda.fwd_workspace_bytes(io, 1, 64, 1, 128, 128, 1, False)
+    full = kda.fwd_workspace_bytes(io, 1, 131072, 32, 128, 128, 1, False)
+    assert full == 2048 * 32 * rec and full > (1 << 32)
+    assert kda.fwd_workspace_min_bytes(io, 1, 131072, 32, 128, 128, 1, False, True) == 32 * rec
+    carry = 32 * 128 * 128 * 4
+    assert kda.fwd_workspace_min_bytes(io, 1, 131072, 32, 128, 128, 1, False, False) == 32 * rec + carry
+    # packed: one chunk index plus one slot per sequence
+    assert kda.fwd_workspace_min_bytes(io, 1, 5000, 2, 128, 128, 3, True, True) == (1 + 3) * 2 * rec
+    # a single chunk per sequence cannot be split
+    assert kda.fwd_workspace_min_bytes(io, 2, 64, 4, 128, 128, 2, False, True) == \
+        kda.fwd_workspace_bytes(io, 2, 64, 4, 128, 128, 2, False)
+    # a workspace between the minimum and one pass is accepted, one byte less than the minimum is not
+    F = 1 << 20
+    L = kda.lib()
+    nmin = kda.fwd_workspace_min_bytes(io, 1, 131072, 32, 128, 128, 1, False, True)
+    assert L.kda_fwd(io, 1, 131072, 32, 128, 128, None, 1, F, F, F, F, F, 1.0, None, F, F, F, nmin - 1, None) == \
+        kda.KDA_ERR_WORKSPACE

@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_93_amd as kda
 import kda_inputs as ki
 import oracle
-from gpu_util import DEV, dev_f32, dev_io, err, host, tol
+from gpu_util import DEV, dev_f32, dev_io, err, err_state, host, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def test_decode_pool_256x32_sampled_chains():
         o_ref, S_ref = oracle.chain(np.stack(rec["q"]), np.stack(rec["k"]), np.stack(rec["v"]),
                                     np.stack(rec["g"]), np.array(rec["b"]), 1.0, S0[n, h])
         worst_o = max(worst_o, err(np.stack(rec["o"]), o_ref, "bf16"))
-        worst_s = max(worst_s, err(S_gpu[n, h], S_ref, "bf16"))
+        worst_s = max(worst_s, err_state(S_gpu[n, h], S_ref, "bf16"))
     print(f"decode 256 x 32 heads: o err {worst_o:.3e}, state err {worst_s:.3e}")
     assert worst_o <= tol("bf16") and worst_s <= tol("bf16")
 
@@ -52,7 +52,7 @@ def test_decode_fp32_equals_recurrence_small():
                             dev_f32(inp.g[:, t]), dev_f32(inp.beta[:, t]), state)
         outs.append(host(o))
     o_gpu = np.stack(outs, axis=1)
-    e_o, e_s = err(o_gpu, o_ref, "f32"), err(host(state), S_ref, "f32")
+    e_o, e_s = err(o_gpu, o_ref, "f32"), err_state(host(state), S_ref, "f32")
     print(f"decode fp32 B1 H2 T256 d64: o err {e_o:.3e}, state err {e_s:.3e}")
     assert e_o <= tol("f32") and e_s <= tol("f32")
 
@@ -77,7 +77,7 @@ def test_decode_shapes(io, dk, dv):
             st = lambda i: np.stack([t[i][n, h] for t in toks])
             o_ref, S_ref = oracle.chain(st(0), st(1), st(2), st(4), np.array([t[3][n, h] for t in toks]), 0.5,
                                         S0[n, h])
-            e = max(err(np.stack([o[n, h] for o in outs]), o_ref, io), err(S_gpu[n, h], S_ref, io))
+            e = max(err(np.stack([o[n, h] for o in outs]), o_ref, io), err_state(S_gpu[n, h], S_ref, io))
             worst = max(worst, e)
     print(f"decode {io} d_k={dk} d_v={dv}: err {worst:.3e}")
     assert worst <= tol(io)

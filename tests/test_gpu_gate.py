@@ -12,7 +12,7 @@ import torch
 import gated_delta_rule_93_amd as kda
 import kda_inputs as ki
 import oracle
-from gpu_util import DEV, dev_f32, dev_io, err, floored_rel, host, rel_inf, tol
+from gpu_util import DEV, dev_f32, dev_io, err, err_state, floored_rel, host, rel_inf, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,7 @@ def check_lowrank(inp, label, chains=None):
     for (n, h), (o_ref, S_ref) in R.run(chains).items():
         bb, s, L = R.bounds(n)
         worst_o = max(worst_o, err(o[bb, s:s + L, h], o_ref, "bf16") if L else 0.0)
-        worst_s = max(worst_s, err(S[n, h], S_ref, "bf16"))
+        worst_s = max(worst_s, err_state(S[n, h], S_ref, "bf16"))
     print(f"low-rank gate fwd {label}: o err {worst_o:.3e}, state err {worst_s:.3e}")
     assert worst_o <= tol("bf16") and worst_s <= tol("bf16"), (label, worst_o, worst_s)
 

@@ -14,7 +14,7 @@ import torch
 import gated_delta_rule_93_amd as kda
 import kda_inputs as ki
 import oracle
-from gpu_util import DEV, dev_f32, dev_io, err, host, tol, upload
+from gpu_util import DEV, dev_f32, dev_io, err, err_state, host, tol, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -93,9 +93,9 @@ def test_prefill_and_decode_steps_replayed_from_a_graph():
             _, S_pf = oracle.chain(qs[:L], ks[:L], vs[:L], gs[:L], bs[:L], 1.0, inp.S0[n, h])
             if L:
                 worst[0] = max(worst[0], err(o_h[0, s0:s0 + L, h], o_ref[:L], "bf16"))
-            worst[1] = max(worst[1], err(S_h[n, h], S_pf, "bf16"))
+            worst[1] = max(worst[1], err_state(S_h[n, h], S_pf, "bf16"))
             worst[2] = max(worst[2], err(np.stack([x[n, h] for x in od_h]), o_ref[L:], "bf16"))
-            worst[3] = max(worst[3], err(st_h[n, h], S_end, "bf16"))
+            worst[3] = max(worst[3], err_state(st_h[n, h], S_end, "bf16"))
     print(f"graph replay vs oracle: prefill o {worst[0]:.2e}, state {worst[1]:.2e}; "
           f"decode o {worst[2]:.2e}, state {worst[3]:.2e}")
     assert max(worst) <= tol("bf16"), worst

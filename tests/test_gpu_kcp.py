@@ -14,7 +14,7 @@ import torch
 import gated_delta_rule_93_amd as kda
 import kda_inputs as ki
 import oracle
-from gpu_util import DEV, dev_f32, dev_io, err, host, rel_inf, tol
+from gpu_util import DEV, dev_f32, dev_io, err, err_state, host, rel_inf, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -49,15 +49,16 @@ def err_A(y, r, io):
 
 def check_maps(inp, cu, label, heads=None):
     A, B = _maps(inp, cu)
-    worst_a = worst_b = 0.0
+    worst_a = worst_b = lit_a = 0.0
     for n in range(len(cu) - 1):
         s, e = int(cu[n]), int(cu[n + 1])
         for h in (range(inp.H) if heads is None else heads):
             A_ref, B_ref = oracle.segment_map(inp.k[0, s:e, h], inp.v[0, s:e, h], inp.g[0, s:e, h],
                                               inp.beta[0, s:e, h])
             worst_a = max(worst_a, err_A(A[n, h], A_ref, inp.io))
-            worst_b = max(worst_b, err(B[n, h], B_ref, inp.io) if e > s else float(np.max(np.abs(B[n, h]))))
-    print(f"segment map {label}: A err {worst_a:.3e}, B err {worst_b:.3e}")
+            lit_a = max(lit_a, err_state(A[n, h], A_ref, inp.io)) if e > s else lit_a
+            worst_b = max(worst_b, err_state(B[n, h], B_ref, inp.io) if e > s else float(np.max(np.abs(B[n, h]))))
+    print(f"segment map {label}: A err {worst_a:.3e} (max|dA|/rms(A) {lit_a:.3e}), B err {worst_b:.3e}")
     assert worst_a <= tol(inp.io) and worst_b <= tol(inp.io), (label, worst_a, worst_b)
 
 
@@ -135,12 +136,10 @@ def test_composed_maps_equal_the_map_of_the_concatenation():
     direct = composed = 0.0
     for h in range(inp.H):
         A_ref, B_ref = oracle.segment_map(inp.k[0, :, h], inp.v[0, :, h], inp.g[0, :, h], inp.beta[0, :, h])
-        direct = max(direct, err_A(host(Aw[0, h]), A_ref, "bf16"), err(host(Bw[0, h]), B_ref, "bf16"))
-        composed = max(composed, err_A(host(A12[h]), A_ref, "bf16"), err(host(B12[h]), B_ref, "bf16"))
+        direct = max(direct, err_A(host(Aw[0, h]), A_ref, "bf16"), err_state(host(Bw[0, h]), B_ref, "bf16"))
+        composed = max(composed, err_A(host(A12[h]), A_ref, "bf16"), err_state(host(B12[h]), B_ref, "bf16"))
     print(f"map of the concatenation: err {direct:.3e}; composed from the two maps: err {composed:.3e}")
-    # each factor is within tol of its reference and has norm <= 1, so the composition (one more
-    # fp32 product) is within the sum of the two factors' errors
-    assert direct <= tol("bf16") and composed <= 2 * tol("bf16")
+    assert direct <= tol("bf16") and composed <= tol("bf16")
 
 
 def run_segmented(inp, seg_lengths):
@@ -161,7 +160,7 @@ def check_segmented(inp, seg_lengths, label, heads=None):
     worst_o = worst_s = 0.0
     for (n, h), (o_ref, S_ref) in R.run(chains).items():
         worst_o = max(worst_o, err(host(o[0, :, h]), o_ref, inp.io))
-        worst_s = max(worst_s, err(host(S[0, h]), S_ref, inp.io))
+        worst_s = max(worst_s, err_state(host(S[0, h]), S_ref, inp.io))
     print(f"segmented {label}: o err {worst_o:.3e}, state err {worst_s:.3e}")
     assert worst_o <= tol(inp.io) and worst_s <= tol(inp.io), (label, worst_o, worst_s)
     return o, S
@@ -175,7 +174,7 @@ def test_segmented_equals_whole_sequence_weak_decay():
     q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
     o1, S1 = kda.fwd(q, k, v, dev_f32(inp.g), dev_f32(inp.beta), 1.0, dev_f32(inp.S0))
     torch.cuda.synchronize()
-    e_o, e_s = err(host(o), host(o1), "bf16"), err(host(S), host(S1), "bf16")
+    e_o, e_s = err(host(o), host(o1), "bf16"), err_state(host(S), host(S1), "bf16")
     print(f"segmented vs unsplit GPU path: o {e_o:.3e}, state {e_s:.3e}")
     # each is within tol of the oracle, so they differ by at most twice that
     assert e_o <= 2 * tol("bf16") and e_s <= 2 * tol("bf16")
@@ -239,7 +238,7 @@ def test_segmented_scalar_gate():
     gb = ki.broadcast_gate(inp.g, inp.q)
     res = oracle.Recurrence(inp.q, inp.k, inp.v, gb, inp.beta, 1.0, inp.S0).run()
     e_o = max(err(host(o[0, :, h]), o_ref, "bf16") for (_, h), (o_ref, _) in res.items())
-    e_s = max(err(host(S[0, h]), S_ref, "bf16") for (_, h), (_, S_ref) in res.items())
+    e_s = max(err_state(host(S[0, h]), S_ref, "bf16") for (_, h), (_, S_ref) in res.items())
     print(f"segmented scalar gate: o err {e_o:.3e}, state err {e_s:.3e}")
     assert e_o <= tol("bf16") and e_s <= tol("bf16")
 
@@ -258,6 +257,6 @@ def test_segmented_lowrank_gate():
     g = oracle.gate_g(inp.z.reshape(B * T, -1), inp.w_up, inp.b, H, d).reshape(B, T, H, d)
     res = oracle.Recurrence(inp.q, inp.k, inp.v, g, inp.beta, 1.0, inp.S0).run()
     e_o = max(err(host(o[0, :, h]), o_ref, "bf16") for (_, h), (o_ref, _) in res.items())
-    e_s = max(err(host(S[0, h]), S_ref, "bf16") for (_, h), (_, S_ref) in res.items())
+    e_s = max(err_state(host(S[0, h]), S_ref, "bf16") for (_, h), (_, S_ref) in res.items())
     print(f"segmented low-rank gate: o err {e_o:.3e}, state err {e_s:.3e}")
     assert e_o <= tol("bf16") and e_s <= tol("bf16")

@@ -10,7 +10,7 @@ import torch
 import gated_delta_rule_93_amd as kda
 import kda_inputs as ki
 import oracle
-from gpu_util import DEV, dev_f32, dev_io, err, host, tol
+from gpu_util import DEV, dev_f32, dev_io, err, err_state, host, tol
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ def check(inp, label, chains=None):
     for (n, h), (o_ref, S_ref) in res.items():
         b, s, L = R.bounds(n)
         worst_o = max(worst_o, err(o[b, s:s + L, h], o_ref, inp.io) if L else 0.0)
-        worst_s = max(worst_s, err(S[n, h], S_ref, inp.io))
+        worst_s = max(worst_s, err_state(S[n, h], S_ref, inp.io))
     print(f"scalar gate {label}: o err {worst_o:.3e}, state err {worst_s:.3e}")
     assert worst_o <= tol(inp.io) and worst_s <= tol(inp.io), (label, worst_o, worst_s)
 
@@ -78,6 +78,6 @@ def test_scalar_gate_equals_per_channel_path():
     q, k, v = (dev_io(x, "bf16") for x in (inp.q, inp.k, inp.v))
     o2, S2 = kda.fwd(q, k, v, dev_f32(ki.broadcast_gate(inp.g, inp.q)), dev_f32(inp.beta), 1.0, dev_f32(inp.S0))
     torch.cuda.synchronize()
-    e_o, e_s = err(o1, host(o2), "bf16"), err(S1, host(S2), "bf16")
+    e_o, e_s = err(o1, host(o2), "bf16"), err_state(S1, host(S2), "bf16")
     print(f"scalar gate vs per-channel path: o {e_o:.3e}, state {e_s:.3e}")
     assert e_o <= tol("bf16") and e_s <= tol("bf16")

@@ -18,10 +18,11 @@ def test_pin(chain_fn, pin):
 
 
 def test_p3_gdn_ordering_is_not_the_adopted_one(chain_fn):
-    """The blog's Gated DeltaNet code reads v_old before decaying; the course page decays first.
-
-    The oracle follows the course page (decay first).  With alpha != 1 the two orders differ;
-    with alpha == 1 they coincide.
+    """Blog post-114 (chapter 3) reads the memory before decaying it in its Gated DeltaNet; the
+    course page (section 3) decays first.  Read-before-decay is the transition
+    S_t = (a_t I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, decay-first the one with
+    a_t (I - beta_t k_t k_t^T).  The oracle follows the course page: with alpha != 1 the two
+    orders differ; with alpha == 1 they coincide.
     """
     rng = np.random.default_rng(3)
     L, dk, dv = 6, 4, 3
@@ -30,14 +31,14 @@ def test_p3_gdn_ordering_is_not_the_adopted_one(chain_fn):
     for a, should_match in ((0.5, False), (1.0, True)):
         g = np.full((L, dk), np.log(a), np.float32)
         S = np.zeros((dk, dv))
-        o_p3 = np.zeros((L, dv))
+        o_read_first = np.zeros((L, dv))
         for t in range(L):
-            kr = k[t:t + 1].astype(np.float64)
-            u = 0.75 * (v[t:t + 1] - kr @ S)
-            S = float(np.exp(g[t, 0])) * S + kr.T @ u
-            o_p3[t] = q[t].astype(np.float64) @ S
+            kt = k[t].astype(np.float64)
+            A = float(np.exp(g[t, 0])) * np.eye(dk) - 0.75 * np.outer(kt, kt)
+            S = A.dot(S) + 0.75 * np.outer(kt, v[t].astype(np.float64))
+            o_read_first[t] = S.T.dot(q[t].astype(np.float64))
         o, _ = chain_fn(q, k, v, g, beta, 1.0, None)
-        assert np.allclose(o, o_p3, rtol=1e-12, atol=1e-12) == should_match
+        assert np.allclose(o, o_read_first, rtol=1e-12, atol=1e-12) == should_match
 
 
 def test_recurrence_wrapper_matches_chain():
