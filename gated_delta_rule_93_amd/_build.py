@@ -14,7 +14,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prep.hip", "kda_chunk.hip", "kda_gate.hip", "kda_attnres.hip",
-           "kda_combine.hip"]
+           "kda_combine.hip", "kda_noalloc.hip"]
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 VALU instructions are kept out of the generated code
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

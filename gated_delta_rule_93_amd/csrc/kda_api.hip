@@ -26,6 +26,9 @@ const char *kda_status_string(kda_status_t s) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: valid arguments that the library does not implement";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
         case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+        case KDA_ERR_TOO_LARGE:
+            return "KDA_ERR_TOO_LARGE: the sizes need more than the library's fixed device scratch "
+                   "(KDA_NOALLOC_SCRATCH_BYTES; kda_fwd_noalloc)";
     }
     return "KDA: unknown status";
 }
@@ -122,6 +125,14 @@ kda::FwdArgs fwd_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, con
 }
 
 }  // namespace
+
+kda_status_t kda::fwd_check_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,
+                                 int N, const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, const float *initial_state, const float *final_state,
+                                 const void *o, const void *workspace, size_t workspace_bytes) {
+    return check_fwd(kBoth, io, B, T, H, d_k, d_v, cu_seqlens, N, q, k, v, g, beta, initial_state, final_state, o,
+                     workspace, workspace_bytes);
+}
 
 extern "C" {
 

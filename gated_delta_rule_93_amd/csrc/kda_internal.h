@@ -8,7 +8,16 @@
 #include <tuple>
 #include <utility>
 
+#include "../../include/kda.h"
+
 namespace kda {
+
+// The argument checks of kda_fwd (sizes, pointers, alignment, workspace against the windowed
+// minimum), without launching anything.
+kda_status_t fwd_check_args(kda_dtype_t io, int B, int T, int H, int d_k, int d_v, const int32_t *cu_seqlens,
+                            int N, const void *q, const void *k, const void *v, const float *g, const float *beta,
+                            const float *initial_state, const float *final_state, const void *o,
+                            const void *workspace, size_t workspace_bytes);
 
 // Launch `kern` on `st` and return the runtime's status for this launch itself (hipLaunchKernel
 // reports it directly; no sticky error left on the thread by an earlier, unrelated call is read

@@ -47,7 +47,8 @@ typedef enum {
     KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned buffer, bad dtype */
     KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k not in {64, 128}) */
     KDA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than kda_fwd_workspace_bytes */
-    KDA_ERR_LAUNCH = 4            /* the HIP runtime rejected a kernel launch */
+    KDA_ERR_LAUNCH = 4,           /* the HIP runtime rejected a kernel launch */
+    KDA_ERR_TOO_LARGE = 5         /* kda_fwd_noalloc: sizes need more than its fixed scratch */
 } kda_status_t;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
@@ -358,6 +359,26 @@ kda_status_t kda_prep(kda_dtype_t io, int B, int T, int H, int d,
                       const int32_t *cu_seqlens, int N,
                       const void *x, const float *conv_w, int W, void *y,
                       hipStream_t stream);
+
+/*
+ * kda_fwd_noalloc -- kda_fwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Arguments as kda_fwd,
+ * without the workspace: the library uses its own fixed device scratch of
+ * KDA_NOALLOC_SCRATCH_BYTES per GPU instead (a device array that each GPU the library runs on
+ * holds until the process ends), running the chunks in windows as large as that scratch allows.
+ * Nothing is allocated or freed.  Returns KDA_ERR_TOO_LARGE, before launching anything, when
+ * even one chunk per window (plus the running states, if final_state is NULL) does not fit,
+ * i.e. when kda_fwd_workspace_min_bytes(...) > KDA_NOALLOC_SCRATCH_BYTES.  All calls on one GPU
+ * share that GPU's scratch: calls that overlap on one GPU (different streams without ordering
+ * between them, or different host threads) race and must not be issued.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+kda_status_t kda_fwd_noalloc(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,
+                             const int32_t *cu_seqlens, int N,
+                             const void *q, const void *k, const void *v,
+                             const float *g, const float *beta, float scale,
+                             const float *initial_state, float *final_state,
+                             void *o, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         s = kda.status_string(code)
         assert s.startswith("KDA_")
     assert "unknown" in kda.status_string(99)
