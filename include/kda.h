@@ -102,13 +102,14 @@ size_t kda_fwd_workspace_min_bytes(kda_dtype_t io, int B, int T, int H, int d_k,
  *   final_state   [N, H, d_k, d_v] fp32 or NULL (not written); may alias initial_state
  *   o             [B, T, H, d_v] io dtype, written for every token; must not alias inputs
  *   workspace     device buffer of at least kda_fwd_workspace_min_bytes(...) bytes (16-byte
- *                 aligned), reused freely by the library during the call.  With
- *                 kda_fwd_workspace_bytes(...) bytes or more every chunk runs in one pass;
- *                 with less, in windows as large as the workspace allows: a dense batch takes
- *                 chunks [w Wc, (w + 1) Wc) of every sequence in window w, a packed batch the
- *                 chunks whose first token lies in [64 w Wc, 64 (w + 1) Wc).  Results are the
- *                 same to rounding (the chunks and their arithmetic do not change; only when
- *                 each is formed), and bitwise the same for any window size on one device.
+ *                 aligned), reused freely by the library during the call.  The chunks run in
+ *                 windows of Wc chunk indices: a dense batch takes chunks [w Wc, (w + 1) Wc) of
+ *                 every sequence in window w, a packed batch the chunks whose first token lies in
+ *                 [64 w Wc, 64 (w + 1) Wc).  With kda_fwd_workspace_bytes(...) bytes or more
+ *                 all chunks run in one window; with less, Wc is as large as the workspace
+ *                 allows.  Results are bitwise the same for any window size on one device (the
+ *                 chunks and their arithmetic do not change, only when each is formed), and equal
+ *                 to kda_fwd_chunk_local + kda_fwd_state_scan.
  *   Returns KDA_ERR_WORKSPACE when workspace is NULL or smaller than the minimum.
  */
 kda_status_t kda_fwd(kda_dtype_t io, int B, int T, int H, int d_k, int d_v,

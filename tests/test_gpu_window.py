@@ -25,6 +25,16 @@ def window_workspace_bytes(io, B, T, H, d, N, varlen, Wc, have_final_state):
     return _align256(nrec * H * rec) + carry
 
 
+def one_pass(inp):
+    """The two phases called on their own: every chunk's record, then the whole scan."""
+    q, k, v, g, beta, S0, cu = upload(inp)
+    io = kda.KDA_BF16 if inp.io == "bf16" else kda.KDA_F32
+    ws = kda.fwd_chunk_local(q, k, v, g, beta, cu)
+    o, S = kda.fwd_state_scan(ws, io, inp.B, inp.T, inp.H, inp.dk, cu, 1.0, S0)
+    torch.cuda.synchronize()
+    return o, S
+
+
 def run(inp, ws_bytes=None, final=True, gate="channel", lowrank=None):
     q, k, v, g, beta, S0, cu = upload(inp)
     ws = None if ws_bytes is None else torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
@@ -53,7 +63,7 @@ def test_windows_equal_one_pass_bitwise(layout, Wc, final):
     inp = _cases()[layout]
     io = kda.KDA_BF16
     varlen = inp.cu_seqlens is not None
-    o1, S1 = run(inp)
+    o1, S1 = one_pass(inp)
     nb = window_workspace_bytes(io, inp.B, inp.T, inp.H, inp.dk, inp.N, varlen, Wc, final)
     assert nb < kda.fwd_workspace_bytes(io, inp.B, inp.T, inp.H, inp.dk, inp.dk, inp.N, varlen)
     o2, S2 = run(inp, nb, final)
@@ -96,9 +106,12 @@ def test_minimum_workspace_against_oracle():
 
 
 def test_prefill_batch_in_windows_bitwise():
-    """The prefill batch (B=4, H=16, T=4096, d=128) in windows of 16 chunks equals the one-pass run."""
+    """The prefill batch (B=4, H=16, T=4096, d=128): kda_fwd with the full workspace and in windows of
+    16 chunks both equal the two phases called on their own."""
     inp = ki.prefill_batch()
-    o1, S1 = run(inp)
+    o1, S1 = one_pass(inp)
+    o2, S2 = run(inp)
     nb = window_workspace_bytes(kda.KDA_BF16, 4, 4096, 16, 128, 4, False, 16, True)
-    o2, S2 = run(inp, nb)
+    o3, S3 = run(inp, nb)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    assert torch.equal(o1, o3) and torch.equal(S1, S3)
