@@ -42,16 +42,20 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Status codes and element types are plain ints across the ABI, so a caller may pass any value
+ * (an unknown dtype or status code is reported, never undefined behaviour). */
+typedef int32_t kda_status_t;
+enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned buffer, bad dtype */
     KDA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. d_k not in {64, 128}) */
     KDA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than kda_fwd_workspace_bytes */
     KDA_ERR_LAUNCH = 4,           /* the HIP runtime rejected a kernel launch */
     KDA_ERR_TOO_LARGE = 5         /* kda_fwd_noalloc: sizes need more than its fixed scratch */
-} kda_status_t;
+};
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+typedef int32_t kda_dtype_t;
+enum { KDA_F32 = 0, KDA_BF16 = 1 };
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *kda_status_string(kda_status_t status);
