@@ -892,12 +892,14 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
 // The operands shared by all tiles (W, Qh, Kh^T, Aqk, e^gamma: one contiguous block at the start
 // of the chunk's workspace record) are copied into LDS by direct global->LDS loads.  Every read
 // of a chunk's block is complete at that chunk's exchange barrier, so with two buffers the copy
-// of chunk c+2 can start right after the exchange barrier of chunk c and has most of two chunk
-// bodies to land.  Two extra waves per workgroup (producers: one for the even chunks, one for
-// the odd ones, so each has at most one chunk in flight and waits for it with vmcnt(0)) issue
-// these copies: a wave stalls while the memory pipeline accepts its loads, and this keeps
-// those stalls off the waves that issue the MFMAs.  When two buffers do not fit, the compute waves copy the next chunk
-// themselves after the current one.  U goes to registers one chunk ahead.  Output rows are
+// of chunk c+2 can start right after the exchange barrier of chunk c.  Two extra waves per
+// workgroup (producers: one for the even chunks, one for the odd ones, so each has at most one
+// chunk in flight and waits for it with vmcnt(0)) issue these copies: a wave stalls while the
+// memory pipeline accepts its loads, and this keeps those stalls off the waves that issue the
+// MFMAs.  Issuing a whole block takes a wave longer than the stretch from an exchange barrier to
+// the next top barrier, so each block is issued in two halves, the second after the next top
+// barrier.  When two buffers do not fit, the compute waves copy the next chunk themselves after
+// the current one.  U goes to registers one chunk ahead.  Output rows are
 // left in LDS and written after the next barrier with 16-byte stores.
 template <bool BF16, int D> struct ScanStage {
     using L = WsLayout<BF16, D>;
@@ -1013,19 +1015,25 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 
     // ================================================================ producer wave
     if (producer) {
-        // all wave-loads of chunk c into buffer BUF
-        auto copy_chunk = [&](long c, auto bufc) __attribute__((always_inline)) {
+        // wave-loads [i0, i1) of chunk c into buffer BUF
+        auto copy_range = [&](long c, auto bufc, int i0, int i1) __attribute__((always_inline)) {
             char *dst = decltype(bufc)::value ? stage1 : stage0;
             const char *src = record(c);
 #pragma unroll
             for (int i = 0; i < St::kLoads; ++i)
-                if (!MAP || map_needs_load<BF16, D>(i)) copy_one(src, dst, i);
+                if (i >= i0 && i < i1 && (!MAP || map_needs_load<BF16, D>(i))) copy_one(src, dst, i);
         };
+        constexpr int kHalf = St::kLoads / 2;
         const int pw = wave - NW;  // this producer copies the chunks c with c % 2 == pw
         if (pw < nck) {
-            if (pw == 0) copy_chunk(0, I0{});
-            else copy_chunk(1, I1{});
+            if (pw == 0) copy_range(0, I0{}, 0, St::kLoads);
+            else copy_range(1, I1{}, 0, St::kLoads);
         }
+        // Chunk c + 2 goes into chunk c's buffer in two halves, so that neither takes longer to
+        // issue than the stretch it has (a wave issues about one 1 KB wave-load per 30-40
+        // clocks): the first after the exchange barrier of chunk c (no wave reads that buffer any
+        // more), the second after the top barrier of chunk c + 1.  The producer waits for both
+        // before the top barrier of chunk c + 2.
         auto pstep = [&](long c, auto bufc) __attribute__((always_inline)) {
             constexpr int buf = decltype(bufc)::value;
             const bool mine = buf == pw;  // chunk c's parity is buf
@@ -1033,9 +1041,11 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             // top barrier without a fence (a fence would make the other producer wait for its
             // copies of the next chunk too)
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // second half of chunk c + 1 (chunks 0 and 1 were copied whole), into the other buffer
+            if (!mine && c >= 1 && c + 1 < nck) copy_range(c + 1, std::integral_constant<int, 1 - buf>{}, kHalf, St::kLoads);
             // exchange barrier: past it, no wave reads this chunk's buffer any more
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (mine && c + 2 < nck) copy_chunk(c + 2, bufc);
+            if (mine && c + 2 < nck) copy_range(c + 2, bufc, 0, kHalf);
         };
         for (long c = 0; c < nck; c += 2) {
             pstep(c, I0{});
