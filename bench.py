@@ -663,9 +663,9 @@ def measured_mfma(workload, kernel):
 # `python bench.py --summarize DIR` turns rocprofv3 csv output into profiles/traffic.json and the
 # text summaries under profiles/.  DIR/<leg>/ holds the output of three runs of one bench leg
 # (<leg> is a name of --only, e.g. prefill, long, varlen, decode, prep):
-#   rocprofv3 --kernel-trace --stats -f csv -d DIR/<leg>/trace -o trace -- python3 bench.py --only <leg>,copy
-#   rocprofv3 --pmc FETCH_SIZE       -f csv -d DIR/<leg>/fetch -o fetch -- python3 bench.py --only <leg>,copy
-#   rocprofv3 --pmc WRITE_SIZE       -f csv -d DIR/<leg>/write -o write -- python3 bench.py --only <leg>,copy
+#   rocprofv3 --kernel-trace --stats -f csv -d DIR/<leg>/trace -o trace -- python3 bench.py --only <leg>,copy --steps 5 --warmup 2
+#   rocprofv3 --pmc FETCH_SIZE       -f csv -d DIR/<leg>/fetch -o fetch -- python3 bench.py --only <leg>,copy --steps 5 --warmup 2
+#   rocprofv3 --pmc WRITE_SIZE       -f csv -d DIR/<leg>/write -o write -- python3 bench.py --only <leg>,copy --steps 5 --warmup 2
 # and optionally DIR/<leg>/mfma (--pmc MfmaUtil MfmaFlopsBF16).  The copy leg runs a 256 MiB
 # device copy in the same process: its FETCH_SIZE / WRITE_SIZE (KiB) against the 268,435,456 bytes
 # it reads and writes give the scale factors applied to every kernel of the leg.
@@ -695,6 +695,9 @@ def _counters(path):
     return per
 
 
+PROFILE_STEPS = "--steps 5 --warmup 2"
+
+
 def summarize_profiles(top, cmd_prefix="rocprofv3"):
     import csv
     copy_name, nb = "__amd_rocclr_copyBuffer", 1 << 28
@@ -706,9 +709,10 @@ def summarize_profiles(top, cmd_prefix="rocprofv3"):
         entry = {"kernels": {}, "mfma": {}, "kernel_avg_us": {}}
         md = [f"# rocprofv3 summary: bench leg `{leg}`", "",
               f"Commands (run from /tmp on one MI355X with TMPDIR=/tmp; `<repo>` is this repository):", "", "```",
-              f"{cmd_prefix} --kernel-trace --stats -f csv -d <out>/{leg}/trace -o trace -- python3 <repo>/bench.py --only {leg},copy",
-              f"{cmd_prefix} --pmc FETCH_SIZE -f csv -d <out>/{leg}/fetch -o fetch -- python3 <repo>/bench.py --only {leg},copy",
-              f"{cmd_prefix} --pmc WRITE_SIZE -f csv -d <out>/{leg}/write -o write -- python3 <repo>/bench.py --only {leg},copy",
+              f"{cmd_prefix} --kernel-trace --stats -f csv -d <out>/{leg}/trace -o trace -- python3 <repo>/bench.py --only {leg},copy {PROFILE_STEPS}",
+              f"{cmd_prefix} --pmc FETCH_SIZE -f csv -d <out>/{leg}/fetch -o fetch -- python3 <repo>/bench.py --only {leg},copy {PROFILE_STEPS}",
+              f"{cmd_prefix} --pmc WRITE_SIZE -f csv -d <out>/{leg}/write -o write -- python3 <repo>/bench.py --only {leg},copy {PROFILE_STEPS}",
+              f"{cmd_prefix} --pmc MfmaUtil MfmaFlopsBF16 -f csv -d <out>/{leg}/mfma -o mfma -- python3 <repo>/bench.py --only {leg} {PROFILE_STEPS}   (prefill, long, varlen)",
               f"python3 <repo>/bench.py --summarize <out>", "```", ""]
         stats = _find_csv(os.path.join(d, "trace"), "kernel_stats.csv")
         if stats:
