@@ -25,8 +25,9 @@
 // chunk takes an exact element-wise fallback instead.
 //
 // Precision (bf16 inputs).  The Gram operands, Tm, Aqk, S and Ud enter the MFMAs as hi + lo
-// bf16 pairs (about 16 significant bits); U stays fp32.  q, k, v are used as stored (exact).
-// The fp32 path uses fp32 MFMAs throughout.
+// bf16 pairs (about 16 significant bits); U stays fp32; Kh^T enters the state update as its bf16
+// plane plus the remainder in fp8 with a per-channel scale (see st_kh).  q, k, v are used as
+// stored (exact).  The fp32 path uses fp32 MFMAs throughout.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -88,11 +89,12 @@ template <> struct Prec<false> {
 
 // ------------------------------------------------------------------ workspace layout
 // Per (chunk slot, head): W, Qh fragments [tt][kb]; Kh^T fragments [rt][kb2]; Aqk fragments
-// (6 lower ones); e^gamma [D] (padded to 1 KB); U as accumulator tiles [jt][tt][lane] f32x4;
-// for bf16, the low half of the hi + lo split of Kh^T [rt][kb2] (its high half is the Kh^T
-// plane above).  Everything before U is read by every column tile of the chain and is staged in
-// LDS by the state scan; U tile jt is read by column tile jt, the Kh^T low plane by each wave
-// for its own state rows.
+// (6 lower ones); e^gamma [D] and, for bf16, the per-channel scale 2^-a of the Kh^T low plane
+// [D] (together padded to 1 KB); U as accumulator tiles [jt][tt][lane] f32x4; for bf16, the low
+// part of Kh^T [rt][kb2] (Kh^T minus its bf16 plane above) as fp8 e4m3 scaled by 2^a per
+// channel, 8 bytes per lane.  Everything before U is read by every column tile of the chain and
+// is staged in LDS by the state scan; U tile jt is read by column tile jt, the Kh^T low plane by
+// each wave for its own state rows.
 template <bool BF16, int D> struct WsLayout {
     static constexpr int NT = 4;           // 16-token tiles per chunk
     static constexpr int NKB = D / 32;     // 32-channel k-blocks
@@ -105,23 +107,56 @@ template <bool BF16, int D> struct WsLayout {
     static constexpr size_t offA = offK + (size_t)nK * PP * 1024;
     static constexpr size_t offE = offA + (size_t)nA * SP * 1024;
     static constexpr size_t offU = offE + 1024;
+    static constexpr size_t offEl = offE + (size_t)D * 4;  // scales of the Kh^T low plane (bf16)
     static constexpr size_t offKl = offU + (size_t)NRT * NT * 1024;
-    static constexpr size_t bytes = offKl + (BF16 ? (size_t)nK * 1024 : 0);
-    static_assert(D * 4 <= 1024, "e^gamma fits its 1 KB slot");
+    static constexpr size_t bytes = offKl + (BF16 ? (size_t)nK * 512 : 0);
+    static_assert(D * 8 <= 1024, "e^gamma and the low-plane scales fit their 1 KB slot");
 };
 
-// Kh^T fragment f of a record: the plain operand in the Kh^T plane and, for bf16, the low half of
-// its hi + lo split in the low plane (the state update takes the split: Kh^T single-rounded to
-// bf16 puts a relative error of 2^-9 on every product, which the state carries).
+// The two Kh^T fragments (row tile rt, token k-blocks 0 and 1) of a record.  fp32: as they are.
+// bf16: the bf16 plane (round to nearest even) and the low part lo = Kh - bf16(Kh) in fp8 e4m3,
+// scaled per channel by 2^a so that the channel's largest |lo| over the chunk's 64 tokens lands in
+// [64, 128) (within the e4m3 range whichever e4m3 variant the hardware uses); 2^-a goes to the
+// record for the state scan.  The state update takes Kh^T as bf16 plane x Ud (hi + lo) plus
+// low part x Ud in bf8: Kh^T single-rounded to bf16 puts a relative error of 2^-9 on every term
+// of Kh^T Ud, which the state carries; with the low part it is about 2^-13.  A channel's 64
+// tokens sit in this lane's two fragments and in the lanes r16 + 16 g of the other lane groups.
 template <bool BF16, int D>
-__device__ __forceinline__ void st_kh(char *wsb, int f, int lane, const float *kh) {
+__device__ __forceinline__ void st_kh(char *wsb, int rt, int lane, const float (&kh)[2][8]) {
     using L = WsLayout<BF16, D>;
     if constexpr (BF16) {
-        const Frag2 s = make_frag2(kh);
-        reinterpret_cast<bf16x8 *>(wsb + L::offK)[f * 64 + lane] = s.h;
-        reinterpret_cast<bf16x8 *>(wsb + L::offKl)[f * 64 + lane] = s.l;
+        float lo[2][8], m = 0.f;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            uint32_t hw[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t h = pk_bf16(kh[kb2][2 * p], kh[kb2][2 * p + 1]);
+                hw[p] = h;
+                lo[kb2][2 * p] = kh[kb2][2 * p] - __uint_as_float(h << 16);
+                lo[kb2][2 * p + 1] = kh[kb2][2 * p + 1] - __uint_as_float(h & 0xffff0000u);
+                m = fmaxf(m, fmaxf(fabsf(lo[kb2][2 * p]), fabsf(lo[kb2][2 * p + 1])));
+            }
+            reinterpret_cast<uint4 *>(wsb + L::offK)[(rt * 2 + kb2) * 64 + lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        // a = 6 - floor(log2 m), within [-126, 126] (m = 0 or tiny: the low part is zero or negligible)
+        const int em = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
+        const int a = m > 0.f ? min(126, max(-126, 6 - em)) : 0;
+        const float up = __uint_as_float((uint32_t)(a + 127) << 23), down = __uint_as_float((uint32_t)(127 - a) << 23);
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][0] * up, lo[kb2][1] * up, 0, false);
+            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][2] * up, lo[kb2][3] * up, w0, true);
+            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][4] * up, lo[kb2][5] * up, 0, false);
+            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][6] * up, lo[kb2][7] * up, w1, true);
+            reinterpret_cast<uint2 *>(wsb + L::offKl)[(rt * 2 + kb2) * 64 + lane] = make_uint2((uint32_t)w0, (uint32_t)w1);
+        }
+        if (lane < 16) reinterpret_cast<float *>(wsb + L::offEl)[16 * rt + lane] = down;
     } else {
-        Prec<false>::st_plain(wsb + L::offK, L::nK, f, lane, make_fragF(kh));
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) Prec<false>::st_plain(wsb + L::offK, L::nK, rt * 2 + kb2, lane, make_fragF(kh[kb2]));
     }
 }
 
@@ -555,20 +590,21 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
         for (int r2 = 0; r2 < 2; ++r2) {
             const int rt = 2 * kb + r2, i = 16 * rt + r16;
             const float gam = sm.g.G[kChunk - 1][i];
+            float kh[2][8];
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
-                float kh[8], xv[8];
+                float xv[8];
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     const int t = 32 * kb2 + kslot(grp, s);
                     const float gt = sm.g.G[t][i];
                     const float kv = IO<TIO>::load(&sm.kq.in.K[t][0], i);
-                    kh[s] = kv * fast_exp2(gam - gt);
+                    kh[kb2][s] = kv * fast_exp2(gam - gt);
                     xv[s] = kv * fast_exp2(gt);
                 }
-                st_kh<BF16, D>(wsb, rt * 2 + kb2, lane, kh);
                 Xf[r2][kb2] = P::plain(xv);
             }
+            st_kh<BF16, D>(wsb, rt, lane, kh);
         }
     }
     if (span_bad) atomicOr(&sm.flag, 1);
@@ -819,20 +855,21 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
 #pragma unroll
         for (int r2 = 0; r2 < 2; ++r2) {
             const int rt = 2 * kb + r2, i = 16 * rt + r16;
+            float kh[2][8];
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) {
-                float eg[8], egm[8], kh[8], xv[8];
+                float eg[8], egm[8], xv[8];
                 ld_kslots(&sm.eG[0], kb2, grp, eg);
                 ld_kslots(&sm.eGm[0], kb2, grp, egm);
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
                     const float kvv = IO<TIO>::load(&sm.kq.in.K[32 * kb2 + kslot(grp, s)][0], i);
-                    kh[s] = kvv * egm[s];
+                    kh[kb2][s] = kvv * egm[s];
                     xv[s] = kvv * eg[s];
                 }
-                st_kh<BF16, D>(wsb, rt * 2 + kb2, lane, kh);
                 Xf[r2][kb2] = P::plain(xv);
             }
+            st_kh<BF16, D>(wsb, rt, lane, kh);
         }
     }
 
@@ -884,11 +921,14 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
 // ------------------------------------------------------------------ kernel 2: state scan
 // A workgroup serves NCT tiles of 16 value columns of one (sequence, head) chain with NS waves
 // per tile (NS = 2 or 4): wave `part` keeps rows part*D/NS .. of the tile's fp32 state in
-// accumulator registers.  Per chunk each wave forms its part of W S and Qh S and publishes them
-// in LDS; every wave adds the parts in the fixed order part 0 + part 1 + ..., so all hold
-// bit-identical Ud.  Each wave then updates its own state rows and forms 4 / NS of the four
-// 16-token output tiles.  Four parts shorten the serial chain per chunk; they are used when the
-// problem has too few tiles to fill the GPU with two-part workgroups.
+// accumulator registers and owns 4 / NS of the chunk's four 16-token tiles.  After every state
+// update each wave splits its rows into hi + lo bf16 operand fragments and publishes them in LDS
+// (sx), so at the next chunk every wave holds the whole state as the B operand: it forms W S and
+// Qh S of its own token tiles over all of d_k, then Ud = U - W S of those tiles, which it splits
+// and publishes (ux).  After the exchange barrier every wave reads all of Ud, updates its own
+// state rows with Kh^T Ud and finishes its output tiles with Aqk Ud.  Four parts shorten the
+// serial chain per chunk; they are used when the problem has too few tiles to fill the GPU with
+// two-part workgroups.
 // The operands shared by all tiles (W, Qh, Kh^T, Aqk, e^gamma: one contiguous block at the start
 // of the chunk's workspace record) are copied into LDS by direct global->LDS loads.  Every read
 // of a chunk's block is complete at that chunk's exchange barrier, so with two buffers the copy
@@ -948,9 +988,13 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     // one buffer from an in-flight copy into the other
     __shared__ __attribute__((aligned(16))) char stage0[St::bytes];
     __shared__ __attribute__((aligned(16))) char stage1[kProd ? St::bytes : 16];
-    __shared__ f32x4 xws[NCT][NS][4][64];  // [tile][from part][token tile][lane]: W S partials
-    // Qh S partials of the tiles a part does not own: [tile][from part][slot][lane]
-    __shared__ f32x4 xqs[MAP ? 1 : NCT][MAP ? 1 : NS][MAP ? 1 : 4 - NOT][64];
+    // the state of each column tile as the B operand of W S and Qh S (hi and lo planes of its
+    // split, k-block fragments), written by the wave that holds the rows after every update
+    __shared__ __attribute__((aligned(16))) char sx[NCT][2 * NKB * 1024];
+    // Ud of each column tile as the B operand of the state update and Aqk Ud (hi and lo planes,
+    // token k-block fragments), each 16-token tile written by the wave that owns it
+    // (bf16: then Ud in bf8 for the Kh^T low plane, 8 bytes per lane and token k-block)
+    __shared__ __attribute__((aligned(16))) char ux[NCT][2 * 2 * 1024 + (BF16 ? 1024 : 0)];
     __shared__ __attribute__((aligned(16))) TIO obuf[kProd && !MAP ? kChunk : 1][kProd && !MAP ? OC : 1];  // output rows
 
     // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
@@ -970,13 +1014,6 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     // four parts tile `part`
     auto own_tile = [&](int i) __attribute__((always_inline)) {
         return NS == 4 ? part : (part ? (i ? 2 : 1) : (i ? 3 : 0));
-    };
-    auto owns = [&](int pp, int tt) __attribute__((always_inline)) {
-        return NS == 4 ? tt == pp : (pp ? (tt == 1 || tt == 2) : (tt == 0 || tt == 3));
-    };
-    // slot of token tile tt among the tiles part pp does not own
-    auto qslot = [&](int pp, int tt) __attribute__((always_inline)) {
-        return NS == 4 ? (tt < pp ? tt : max(tt - 1, 0)) : (tt >> 1);
     };
 
     // this chain's chunks in window `win` (see Window): [c_lo, c_hi); the state enters from s0 in
@@ -1084,18 +1121,18 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             if (i < St::kLoads && (!MAP || map_needs_load<BF16, D>(i))) copy_one(record(c), stage0, i);
         }
     };
-    // U tiles alternate between two register sets (even chunks in uA, odd in uB), so a
-    // prefetched tile is never copied between registers before it has arrived
-    f32x4 uA[4], uB[4];
-    auto prefetch_u = [&](long c, f32x4 (&u)[4]) __attribute__((always_inline)) {
+    // U of the own token tiles; the tiles alternate between two register sets (even chunks in
+    // uA, odd in uB), so a prefetched tile is never copied between registers before it has arrived
+    f32x4 uA[NOT], uB[NOT];
+    auto prefetch_u = [&](long c, f32x4 (&u)[NOT]) __attribute__((always_inline)) {
         if (amap) {  // the linear part: U is zero
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) u[tt] = zero4();
+            for (int i = 0; i < NOT; ++i) u[i] = zero4();
             return;
         }
         const f32x4 *pu = reinterpret_cast<const f32x4 *>(record(c) + L::offU) + jt * 4 * 64 + lane;
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) u[tt] = pu[tt * 64];
+        for (int i = 0; i < NOT; ++i) u[i] = pu[own_tile(i) * 64];
     };
 
     f32x4 S[RTH];
@@ -1107,6 +1144,17 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             S[r][e] = MAP ? (amap && 16 * (part * RTH + r) + 4 * grp + e == col ? 1.f : 0.f)
                           : sin ? sin[sbase + (long)(16 * (part * RTH + r) + 4 * grp + e) * D + col] : 0.f;
 
+    // this wave's rows of the state, split, into sx (k-blocks part * KBH ..); the next top barrier
+    // publishes them
+    auto publish_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < KBH; ++kk) {
+            float vals[8] = {S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3],
+                             S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
+            P::st_split(&sx[ct][0], NKB, part * KBH + kk, lane, P::split(vals));
+        }
+    };
+    publish_state();
     if (nck > 0) {
         if (!kProd) stage_all(0);
         prefetch_u(0, uA);
@@ -1114,59 +1162,79 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     // One chunk.  The buffer index is a compile-time constant (the loop below is unrolled by
     // two), so the compiler can tell the LDS reads of this chunk from the copies into the
     // other buffer and does not make the reads wait for those copies.
-    auto chunk_step = [&](long c, auto bufc, f32x4 (&u_cur)[4], f32x4 (&u_nx)[4]) __attribute__((always_inline)) {
+    auto chunk_step = [&](long c, auto bufc, f32x4 (&u_cur)[NOT], f32x4 (&u_nx)[NOT]) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
-        __syncthreads();                // ... and every copy: chunk c is in LDS
+        __syncthreads();                // ... and every copy: chunk c is in LDS, and so is the state
         const bool more = c + 1 < nck;
         const char *sb = buf ? stage1 : stage0;
-        // W and Qh fragments of this part; bf16 ones are all requested before the first product
-        // (fp32 ones take twice the registers and are read next to their use)
-        auto ldW = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offW, L::nW, tt * NKB + part * KBH + kk, lane); };
-        auto ldQ = [&](int tt, int kk) __attribute__((always_inline)) { return P::ld_plain(sb + L::offQ, L::nQ, tt * NKB + part * KBH + kk, lane); };
-        Plain wf[4][KBH], qf[4][KBH];
-        if (BF16) {
+        // the state (every k-block) and the W and Qh fragments of the own token tiles; bf16 ones are
+        // all requested before the first product (fp32 ones take twice the registers and are read
+        // next to their use)
+        const char *sxb = &sx[ct][0];
+        auto ldS = [&](int kb) __attribute__((always_inline)) { return P::ld_split(sxb, NKB, kb, lane); };
+        auto ldW = [&](int i, int kb) __attribute__((always_inline)) { return P::ld_plain(sb + L::offW, L::nW, own_tile(i) * NKB + kb, lane); };
+        auto ldQ = [&](int i, int kb) __attribute__((always_inline)) { return P::ld_plain(sb + L::offQ, L::nQ, own_tile(i) * NKB + kb, lane); };
+        Split sop[BF16 ? NKB : 1];
+        Plain wf[NOT][BF16 ? NKB : 1], qf[NOT][BF16 ? NKB : 1];
+        if constexpr (BF16) {
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+            for (int kb = 0; kb < NKB; ++kb) {
+                sop[kb] = ldS(kb);
 #pragma unroll
-                for (int kk = 0; kk < KBH; ++kk) {
-                    wf[tt][kk] = ldW(tt, kk);
-                    if constexpr (!MAP) qf[tt][kk] = ldQ(tt, kk);
+                for (int i = 0; i < NOT; ++i) {
+                    wf[i][kb] = ldW(i, kb);
+                    if constexpr (!MAP) qf[i][kb] = ldQ(i, kb);
                 }
+            }
         }
         if (more) prefetch_u(c + 1, u_nx);
-        // low plane of this part's Kh^T rows (bf16): straight from the record, used after the
-        // exchange barrier
-        FragB kl[BF16 ? RTH : 1][2];
+        // low plane of this part's Kh^T rows (bf16, fp8 e4m3): straight from the record, used
+        // after the exchange barrier
+        long kl[BF16 ? RTH : 1][2];
         if constexpr (BF16) {
-            const bf16x8 *pk = reinterpret_cast<const bf16x8 *>(record(c) + L::offKl) + lane;
+            const long *pk = reinterpret_cast<const long *>(record(c) + L::offKl) + lane;
 #pragma unroll
             for (int r = 0; r < RTH; ++r)
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2) kl[r][kb2].h = pk[((part * RTH + r) * 2 + kb2) * 64];
+                for (int kb2 = 0; kb2 < 2; ++kb2) kl[r][kb2] = pk[((part * RTH + r) * 2 + kb2) * 64];
         }
-        // this part's contribution to W S and Qh S, one k-block at a time (the split of the next
-        // block's state rows can then issue while the products of this one run); every tile still
-        // sums its k-blocks in the same order
-        f32x4 wsa[4], qsa[4];
+        // W S and Qh S of the own token tiles over all of d_k, k-blocks in order
+        f32x4 wsa[NOT], qsa[NOT];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) { wsa[tt] = zero4(); qsa[tt] = zero4(); }
+        for (int i = 0; i < NOT; ++i) { wsa[i] = zero4(); qsa[i] = zero4(); }
 #pragma unroll
-        for (int kk = 0; kk < KBH; ++kk) {
-            float vals[8] = {S[2 * kk][0], S[2 * kk][1], S[2 * kk][2], S[2 * kk][3],
-                             S[2 * kk + 1][0], S[2 * kk + 1][1], S[2 * kk + 1][2], S[2 * kk + 1][3]};
-            const Split sop = P::split(vals);
+        for (int kb = 0; kb < NKB; ++kb) {
+            const Split so = BF16 ? sop[BF16 ? kb : 0] : ldS(kb);
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                wsa[tt] = mfma(BF16 ? wf[tt][kk] : ldW(tt, kk), sop, wsa[tt]);
-                if constexpr (!MAP) qsa[tt] = mfma(BF16 ? qf[tt][kk] : ldQ(tt, kk), sop, qsa[tt]);
+            for (int i = 0; i < NOT; ++i) {
+                wsa[i] = mfma(BF16 ? wf[i][BF16 ? kb : 0] : ldW(i, kb), so, wsa[i]);
+                if constexpr (!MAP) qsa[i] = mfma(BF16 ? qf[i][BF16 ? kb : 0] : ldQ(i, kb), so, qsa[i]);
             }
         }
+        // Ud = U - W S of the own tiles, split, into ux (tile tt fills half tt & 1 of token
+        // k-block tt >> 1 in both planes)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            xws[ct][part][tt][lane] = wsa[tt];
-            if constexpr (!MAP)
-                if (!owns(part, tt)) xqs[ct][part][qslot(part, tt)][lane] = qsa[tt];
+        for (int i = 0; i < NOT; ++i) {
+            const int ot = own_tile(i);
+            const f32x4 ud = u_cur[i] - wsa[i];
+            char *dst = &ux[ct][0] + ((ot >> 1) * 64 + lane) * 16;
+            if constexpr (BF16) {
+                const uint32_t h01 = pk_bf16(ud[0], ud[1]), h23 = pk_bf16(ud[2], ud[3]);
+                const uint32_t l01 = pk_bf16(ud[0] - __uint_as_float(h01 << 16), ud[1] - __uint_as_float(h01 & 0xffff0000u));
+                const uint32_t l23 = pk_bf16(ud[2] - __uint_as_float(h23 << 16), ud[3] - __uint_as_float(h23 & 0xffff0000u));
+                *reinterpret_cast<uint2 *>(dst + (ot & 1) * 8) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2 *>(dst + 2048 + (ot & 1) * 8) = make_uint2(l01, l23);
+                // bf8 (clamped to its largest finite value) for the Kh^T low plane
+                float c8[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c8[e] = fminf(fmaxf(ud[e], -57344.f), 57344.f);
+                int w8 = __builtin_amdgcn_cvt_pk_bf8_f32(c8[0], c8[1], 0, false);
+                w8 = __builtin_amdgcn_cvt_pk_bf8_f32(c8[2], c8[3], w8, true);
+                *reinterpret_cast<int *>(&ux[ct][0] + 4096 + ((ot >> 1) * 64 + lane) * 8 + (ot & 1) * 4) = w8;
+            } else {
+                *reinterpret_cast<f32x4 *>(dst + (ot & 1) * 2048) = ud;
+            }
         }
         // operands of the second part of the chunk, requested before the barrier
         // (with a producer the buffer is refilled right after the exchange barrier, so every
@@ -1190,10 +1258,12 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
                 af[i][1] = P::ld_split(sb + L::offA, L::nA, aidx(ot, ot >= 2 ? 1 : 0), lane);
             }
         }
-        f32x4 e_cur[RTH];
+        f32x4 e_cur[RTH], e_lo[BF16 ? RTH : 1];
 #pragma unroll
-        for (int r = 0; r < RTH; ++r)
+        for (int r = 0; r < RTH; ++r) {
             e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (part * RTH + r) + 4 * grp));
+            if constexpr (BF16) e_lo[r] = *reinterpret_cast<const f32x4 *>(sb + L::offEl + 4 * (16 * (part * RTH + r) + 4 * grp));
+        }
         // rows of the previous chunk (left in obuf before the top barrier; refilled after the
         // exchange barrier)
         if constexpr (!MAP)
@@ -1201,42 +1271,36 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         // exchange barrier: only LDS traffic must be complete (lgkmcnt); copies into the other
         // stage buffer stay in flight (a fence here would wait for them too)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // Ud = U - (W S [part 0] + W S [part 1] + ...), every wave in the same order
-        f32x4 ud[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            f32x4 sum = xws[ct][0][tt][lane];
-#pragma unroll
-            for (int pp = 1; pp < NS; ++pp) sum += xws[ct][pp][tt][lane];
-            ud[tt] = u_cur[tt] - sum;
-        }
+        // Ud of all four token tiles (every wave reads the same split values)
         Split Uop[2];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            float vals[8] = {ud[2 * kb2][0], ud[2 * kb2][1], ud[2 * kb2][2], ud[2 * kb2][3],
-                             ud[2 * kb2 + 1][0], ud[2 * kb2 + 1][1], ud[2 * kb2 + 1][2], ud[2 * kb2 + 1][3]};
-            Uop[kb2] = P::split(vals);
-        }
-        // O rows of the own tiles (Qh S summed over the parts in part order, then Aqk Ud) and
-        // the state update; the products that need only the first k-block of Ud come first
+        for (int kb2 = 0; kb2 < 2; ++kb2) Uop[kb2] = P::ld_split(&ux[ct][0], 2, kb2, lane);
+        // O rows of the own tiles (Qh S, then Aqk Ud) and the state update; the products that
+        // need only the first token k-block of Ud come first
         f32x4 oo[NOT], Sn[RTH];
 #pragma unroll
-        for (int i = 0; i < (MAP ? 0 : NOT); ++i) {
-            const int ot = own_tile(i);
-            const f32x4 mine = ot == 0 ? qsa[0] : ot == 1 ? qsa[1] : ot == 2 ? qsa[2] : qsa[3];
-            oo[i] = part == 0 ? mine : xqs[ct][0][qslot(0, ot)][lane];
-#pragma unroll
-            for (int pp = 1; pp < NS; ++pp) oo[i] += pp == part ? mine : xqs[ct][pp][qslot(pp, ot)][lane];
-        }
+        for (int i = 0; i < NOT; ++i) oo[i] = qsa[i];
 #pragma unroll
         for (int r = 0; r < RTH; ++r) Sn[r] = S[r] * e_cur[r];
+        if constexpr (BF16) {
+            // the Kh^T low plane times Ud in bf8, scaled back per state row
+            long u8[2];
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) u8[kb2] = *reinterpret_cast<const long *>(&ux[ct][0] + 4096 + (kb2 * 64 + lane) * 8);
+#pragma unroll
+            for (int r = 0; r < RTH; ++r) {
+                f32x4 a8 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_bf8(kl[r][0], u8[0], zero4(), 0, 0, 0);
+                a8 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_bf8(kl[r][1], u8[1], a8, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Sn[r][e] = fmaf(a8[e], e_lo[r][e], Sn[r][e]);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < (MAP ? 0 : NOT); ++i) oo[i] = mfma(af[i][0], Uop[0], oo[i]);
-        // Kh^T as the state update takes it: hi + lo for bf16, fp32 as stored otherwise
+        // Kh^T as the state update takes it: its bf16 plane (the low plane was added above), fp32
+        // as stored otherwise
         auto khop = [&](int r, int kb2) __attribute__((always_inline)) {
-            const Plain hi = kEarlyK ? kf[r][kb2] : ldK(r, kb2);
-            if constexpr (BF16) return Frag2{hi.h, kl[r][kb2].h};
-            else return hi;
+            return kEarlyK ? kf[r][kb2] : ldK(r, kb2);
         };
 #pragma unroll
         for (int r = 0; r < RTH; ++r) Sn[r] = mfma(khop(r, 0), Uop[0], Sn[r]);
@@ -1245,6 +1309,8 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             if (own_tile(i) >= 2) oo[i] = mfma(af[i][1], Uop[1], oo[i]);
 #pragma unroll
         for (int r = 0; r < RTH; ++r) S[r] = mfma(khop(r, 1), Uop[1], Sn[r]);
+        // every read of sx for this chunk was complete at the exchange barrier
+        publish_state();
         if (kProd) {
             // rows of this chunk (the previous ones were read before the exchange barrier)
 #pragma unroll

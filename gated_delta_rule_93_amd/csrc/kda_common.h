@@ -99,16 +99,27 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
 }
 
 __device__ __forceinline__ FragB make_fragB(const float *x) { return FragB{to_bf16x8(x)}; }
+
+// Two fp32 values rounded to nearest-even bf16, packed (a in the low half): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// hi = bf16(x), lo = bf16(x - hi), element by element.  Written per pair so that the rounded pair
+// is converted once and its two values are read back from the packed word (a shift and a mask).
 __device__ __forceinline__ Frag2 make_frag2(const float *x) {
-    Frag2 f;
-    float lo[8];
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        __bf16 h = (__bf16)x[s];
-        f.h[s] = h;
-        lo[s] = x[s] - (float)h;
+    for (int p = 0; p < 4; ++p) {
+        const uint32_t h = pk_bf16(x[2 * p], x[2 * p + 1]);
+        const float f0 = __uint_as_float(h << 16), f1 = __uint_as_float(h & 0xffff0000u);
+        hw[p] = h;
+        lw[p] = pk_bf16(x[2 * p] - f0, x[2 * p + 1] - f1);
     }
-    f.l = to_bf16x8(lo);
+    Frag2 f;
+    f.h = __builtin_bit_cast(bf16x8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+    f.l = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
     return f;
 }
 __device__ __forceinline__ FragF make_fragF(const float *x) {
