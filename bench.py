@@ -53,7 +53,7 @@ PREFILL_BYTES = PREFILL_IN_BYTES + PREFILL_OUT_BYTES   # 1,540 B per token-head
 PREFILL_FLOP = 140.5e3
 # kernel names as rocprofv3 reports them
 K_LOCAL = "kda::chunk_local_kernel<true, 128, false>"
-K_SCAN_2T = "kda::chunk_scan_kernel<true, 128, 2, 2, false>"   # two column tiles per workgroup
+K_SCAN_2T = "kda::chunk_scan_kernel<true, 128, 2, 4, false>"   # two column tiles per workgroup
 K_SCAN_1T = "kda::chunk_scan_kernel<true, 128, 1, 4, false>"   # one tile, four waves (few chains)
 K_DECODE = "kda::decode_step_kernel<unsigned short, 128, 128>"
 K_PREP = "kda::prep_kernel<unsigned short, 128, 4>"

@@ -1448,19 +1448,19 @@ static int device_cu_count() {
 }
 
 // Column tiles per workgroup: two when that still gives every CU a workgroup (the tiles then
-// share one LDS copy of the chunk's operands), else one with the state split over more waves.
-// The segment map (MAP) has twice the column tiles: those of B and those of A.
+// share one LDS copy of the chunk's operands), else one.  At d = 128 four waves per tile (a
+// shorter serial chain per chunk than two; the results are bitwise the same, since every wave
+// forms its products over all of d_k in the same order), at d = 64 two.  The segment map (MAP)
+// has twice the column tiles: those of B and those of A.
 template <bool BF16, int D, bool MAP = false>
 static hipError_t launch_scan_t(const FwdArgs &a, const Window &win, hipStream_t st) {
     const int nchains = a.N * a.H;
     if (nchains <= 0) return hipSuccess;
     const int cus = device_cu_count();
     const long tiles = (long)nchains * (D / 16) * (MAP ? 2 : 1);
-    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2, 2, MAP>(a, win, st, nchains);
-    // too few tiles to give every CU a two-tile workgroup: one tile per workgroup, and at
-    // d = 128 four waves per tile (a shorter serial chain per chunk)
-    if constexpr (D == 128) return launch_scan_nct<BF16, D, 1, 4, MAP>(a, win, st, nchains);
-    else return launch_scan_nct<BF16, D, 1, 2, MAP>(a, win, st, nchains);
+    constexpr int NS = D == 128 ? 4 : 2;
+    if (tiles / 2 >= cus) return launch_scan_nct<BF16, D, 2, NS, MAP>(a, win, st, nchains);
+    return launch_scan_nct<BF16, D, 1, NS, MAP>(a, win, st, nchains);
 }
 
 template <bool BF16, int D>
