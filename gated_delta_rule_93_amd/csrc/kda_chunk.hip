@@ -90,7 +90,8 @@ template <> struct Prec<false> {
 // ------------------------------------------------------------------ workspace layout
 // Per (chunk slot, head): W, Qh fragments [tt][kb]; Kh^T fragments [rt][kb2]; Aqk fragments
 // (6 lower ones); e^gamma [D] and, for bf16, the per-channel scale 2^-a of the Kh^T low plane
-// [D] (together padded to 1 KB); U as accumulator tiles [jt][tt][lane] f32x4; for bf16, the low
+// [D] (together padded to 1 KB); U as accumulator tiles [jt][tt][lane] (f32x4; for bf16 the four
+// values as 24-bit floats in three dwords, see pack_u24); for bf16, the low
 // part of Kh^T [rt][kb2] (Kh^T minus its bf16 plane above) as fp8 e4m3 scaled by 2^a per
 // channel, 8 bytes per lane.  Everything before U is read by every column tile of the chain and
 // is staged in LDS by the state scan; U tile jt is read by column tile jt, the Kh^T low plane by
@@ -108,7 +109,8 @@ template <bool BF16, int D> struct WsLayout {
     static constexpr size_t offE = offA + (size_t)nA * SP * 1024;
     static constexpr size_t offU = offE + 1024;
     static constexpr size_t offEl = offE + (size_t)D * 4;  // scales of the Kh^T low plane (bf16)
-    static constexpr size_t offKl = offU + (size_t)NRT * NT * 1024;
+    static constexpr size_t uTile = BF16 ? 768 : 1024;   // bytes of one U accumulator tile
+    static constexpr size_t offKl = offU + (size_t)NRT * NT * uTile;
     static constexpr size_t bytes = offKl + (BF16 ? (size_t)nK * 512 : 0);
     static_assert(D * 8 <= 1024, "e^gamma and the low-plane scales fit their 1 KB slot");
 };
@@ -158,6 +160,27 @@ __device__ __forceinline__ void st_kh(char *wsb, int rt, int lane, const float (
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) Prec<false>::st_plain(wsb + L::offK, L::nK, rt * 2 + kb2, lane, make_fragF(kh[kb2]));
     }
+}
+
+// U of the bf16 path in 24-bit floats: fp32 rounded to nearest even at 15 stored mantissa bits
+// (relative error 2^-16, far below what the bf16 W of U - W S brings), four values in the three
+// high bytes of each, three dwords per lane.  v_perm_b32 takes bytes 0-3 from its second operand
+// and 4-7 from its first; selector 0x0c gives a zero byte.
+struct U24 { uint32_t w0, w1, w2; };
+__device__ __forceinline__ U24 pack_u24(f32x4 x) {
+    uint32_t r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t u = __float_as_uint(x[e]);
+        r[e] = u + 0x7fu + ((u >> 8) & 1u);
+    }
+    return U24{__builtin_amdgcn_perm(r[1], r[0], 0x05030201u), __builtin_amdgcn_perm(r[2], r[1], 0x06050302u),
+               __builtin_amdgcn_perm(r[3], r[2], 0x07060503u)};
+}
+__device__ __forceinline__ f32x4 unpack_u24(const U24 &w) {
+    return f32x4{__uint_as_float(__builtin_amdgcn_perm(w.w0, w.w0, 0x0201000cu)),
+                 __uint_as_float(__builtin_amdgcn_perm(w.w1, w.w0, 0x0504030cu)),
+                 __uint_as_float(__builtin_amdgcn_perm(w.w2, w.w1, 0x0403020cu)), __uint_as_float(w.w2 & 0xffffff00u)};
 }
 
 // lower Aqk fragment index of (token tile tt, token k-block kb2), kb2 <= tt / 2
@@ -412,7 +435,8 @@ __device__ __forceinline__ void ut_and_outputs(SM &sm, const Raw4<typename SM::T
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc = mfma(Tf[aidx(tt, kb2)], Vf[kb2], acc);
-            reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
+            if constexpr (BF16) reinterpret_cast<U24 *>(wsb + L::offU)[(jt * 4 + tt) * 64 + lane] = pack_u24(acc);
+            else reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
         }
     }
 }
@@ -1123,16 +1147,21 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     };
     // U of the own token tiles; the tiles alternate between two register sets (even chunks in
     // uA, odd in uB), so a prefetched tile is never copied between registers before it has arrived
-    f32x4 uA[NOT], uB[NOT];
-    auto prefetch_u = [&](long c, f32x4 (&u)[NOT]) __attribute__((always_inline)) {
+    using UT = typename std::conditional<BF16, U24, f32x4>::type;  // a U tile as stored
+    UT uA[NOT], uB[NOT];
+    auto prefetch_u = [&](long c, UT (&u)[NOT]) __attribute__((always_inline)) {
         if (amap) {  // the linear part: U is zero
 #pragma unroll
-            for (int i = 0; i < NOT; ++i) u[i] = zero4();
+            for (int i = 0; i < NOT; ++i) u[i] = UT{};
             return;
         }
-        const f32x4 *pu = reinterpret_cast<const f32x4 *>(record(c) + L::offU) + jt * 4 * 64 + lane;
+        const UT *pu = reinterpret_cast<const UT *>(record(c) + L::offU) + jt * 4 * 64 + lane;
 #pragma unroll
         for (int i = 0; i < NOT; ++i) u[i] = pu[own_tile(i) * 64];
+    };
+    auto u_value = [&](const UT &u) __attribute__((always_inline)) {
+        if constexpr (BF16) return unpack_u24(u);
+        else return u;
     };
 
     f32x4 S[RTH];
@@ -1162,7 +1191,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     // One chunk.  The buffer index is a compile-time constant (the loop below is unrolled by
     // two), so the compiler can tell the LDS reads of this chunk from the copies into the
     // other buffer and does not make the reads wait for those copies.
-    auto chunk_step = [&](long c, auto bufc, f32x4 (&u_cur)[NOT], f32x4 (&u_nx)[NOT]) __attribute__((always_inline)) {
+    auto chunk_step = [&](long c, auto bufc, UT (&u_cur)[NOT], UT (&u_nx)[NOT]) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
         __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
         __syncthreads();                // ... and every copy: chunk c is in LDS, and so is the state
@@ -1217,7 +1246,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
 #pragma unroll
         for (int i = 0; i < NOT; ++i) {
             const int ot = own_tile(i);
-            const f32x4 ud = u_cur[i] - wsa[i];
+            const f32x4 ud = u_value(u_cur[i]) - wsa[i];
             char *dst = &ux[ct][0] + ((ot >> 1) * 64 + lane) * 16;
             if constexpr (BF16) {
                 const uint32_t h01 = pk_bf16(ud[0], ud[1]), h23 = pk_bf16(ud[2], ud[3]);
