@@ -1019,6 +1019,12 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
     // token k-block fragments), each 16-token tile written by the wave that owns it
     // (bf16: then Ud in bf8 for the Kh^T low plane, 8 bytes per lane and token k-block)
     __shared__ __attribute__((aligned(16))) char ux[NCT][2 * 2 * 1024 + (BF16 ? 1024 : 0)];
+    // the Kh^T low plane of the current chunk (bf16 with producer waves): loaded into registers by
+    // the chunk's producer with its stage copies, written here after the chunk's top barrier, read
+    // after its exchange barrier
+    constexpr bool kKlx = BF16 && kProd;
+    constexpr int kKlFrags = L::nK;  // fragments of 512 bytes
+    __shared__ __attribute__((aligned(16))) long klx[kKlx ? kKlFrags * 64 : 1];
     __shared__ __attribute__((aligned(16))) TIO obuf[kProd && !MAP ? kChunk : 1][kProd && !MAP ? OC : 1];  // output rows
 
     // the GPC workgroups of one chain go to the same XCD (blocks are dealt round-robin to 8 XCDs)
@@ -1086,9 +1092,18 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         };
         constexpr int kHalf = St::kLoads / 2;
         const int pw = wave - NW;  // this producer copies the chunks c with c % 2 == pw
+        long klr[kKlx ? kKlFrags : 1];  // the low plane of this producer's next chunk
+        auto load_kl = [&](long c) __attribute__((always_inline)) {
+            if constexpr (kKlx) {
+                const long *pk = reinterpret_cast<const long *>(record(c) + L::offKl) + lane;
+#pragma unroll
+                for (int f = 0; f < kKlFrags; ++f) klr[f] = pk[f * 64];
+            }
+        };
         if (pw < nck) {
             if (pw == 0) copy_range(0, I0{}, 0, St::kLoads);
             else copy_range(1, I1{}, 0, St::kLoads);
+            load_kl(pw);
         }
         // Chunk c + 2 goes into chunk c's buffer in two halves, so that neither takes longer to
         // issue than the stretch it has (a wave issues about one 1 KB wave-load per 30-40
@@ -1102,11 +1117,21 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             // top barrier without a fence (a fence would make the other producer wait for its
             // copies of the next chunk too)
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            // chunk c's low plane into LDS (every read of chunk c - 1's was done before this barrier;
+            // the exchange barrier below publishes it)
+            if constexpr (kKlx)
+                if (mine) {
+#pragma unroll
+                    for (int f = 0; f < kKlFrags; ++f) klx[f * 64 + lane] = klr[f];
+                }
             // second half of chunk c + 1 (chunks 0 and 1 were copied whole), into the other buffer
             if (!mine && c >= 1 && c + 1 < nck) copy_range(c + 1, std::integral_constant<int, 1 - buf>{}, kHalf, St::kLoads);
             // exchange barrier: past it, no wave reads this chunk's buffer any more
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            if (mine && c + 2 < nck) copy_range(c + 2, bufc, 0, kHalf);
+            if (mine && c + 2 < nck) {
+                copy_range(c + 2, bufc, 0, kHalf);
+                load_kl(c + 2);
+            }
         };
         for (long c = 0; c < nck; c += 2) {
             pstep(c, I0{});
@@ -1218,10 +1243,10 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
             }
         }
         if (more) prefetch_u(c + 1, u_nx);
-        // low plane of this part's Kh^T rows (bf16, fp8 e4m3): straight from the record, used
-        // after the exchange barrier
+        // low plane of this part's Kh^T rows (bf16, fp8 e4m3), used after the exchange barrier:
+        // from LDS where the producer put it, else straight from the record
         long kl[BF16 ? RTH : 1][2];
-        if constexpr (BF16) {
+        if constexpr (BF16 && !kKlx) {
             const long *pk = reinterpret_cast<const long *>(record(c) + L::offKl) + lane;
 #pragma unroll
             for (int r = 0; r < RTH; ++r)
@@ -1311,6 +1336,12 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchai
         for (int i = 0; i < NOT; ++i) oo[i] = qsa[i];
 #pragma unroll
         for (int r = 0; r < RTH; ++r) Sn[r] = S[r] * e_cur[r];
+        if constexpr (kKlx) {
+#pragma unroll
+            for (int r = 0; r < RTH; ++r)
+#pragma unroll
+                for (int kb2 = 0; kb2 < 2; ++kb2) kl[r][kb2] = klx[((part * RTH + r) * 2 + kb2) * 64 + lane];
+        }
         if constexpr (BF16) {
             // the Kh^T low plane times Ud in bf8, scaled back per state row
             long u8[2];
