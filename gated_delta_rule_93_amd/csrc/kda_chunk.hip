@@ -15,8 +15,8 @@
 //   It builds the cumulative log-decay in LDS, the two decayed Gram matrices, the UT
 //   transform Tm by blocked forward substitution, and writes W, U, Qh, Kh^T, Aqk and
 //   e^gamma to the workspace, laid out as ready-to-load MFMA operand fragments.
-// Kernel 2 (chunk_scan_kernel): one wave per (sequence, head, 16 value columns); it keeps its
-//   d_k x 16 slice of the fp32 state in MFMA accumulator registers and walks the chunks.
+// Kernel 2 (chunk_scan_kernel): per (sequence, head, 16 value columns) a set of 2 or 4 waves, each
+//   keeping a slice of the d_k x 16 fp32 state in MFMA accumulator registers, walks the chunks.
 //
 // Exponent safety.  Every e^{x} is evaluated with x <= 0 or with |x| bounded by a checked
 // half-span: the Gram matrices use 16-token sub-blocks with the sub-block's middle row m as
@@ -25,9 +25,9 @@
 // chunk takes an exact element-wise fallback instead.
 //
 // Precision (bf16 inputs).  The Gram operands, Tm, Aqk, S and Ud enter the MFMAs as hi + lo
-// bf16 pairs (about 16 significant bits); U stays fp32; Kh^T enters the state update as its bf16
-// plane plus the remainder in fp8 with a per-channel scale (see st_kh).  q, k, v are used as
-// stored (exact).  The fp32 path uses fp32 MFMAs throughout.
+// bf16 pairs (about 16 significant bits); U is kept at 24 bits (see pack_u24); Kh^T enters the
+// state update as its bf16 plane plus the remainder in fp8 with a per-channel scale (see st_kh).
+// q, k, v are used as stored (exact).  The fp32 path uses fp32 MFMAs and fp32 U throughout.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
