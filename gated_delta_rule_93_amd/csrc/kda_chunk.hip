@@ -465,7 +465,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     using L = WsLayout<BF16, D>;
     using Plain = typename P::Plain;
     using Split = typename P::Split;
-    constexpr int NKB = L::NKB, NRT = L::NRT;
+    constexpr int NKB = L::NKB;
     __shared__ ChunkSmem<BF16, D> sm;
 
     long rec;
@@ -990,7 +990,7 @@ template <bool BF16, int D> constexpr bool map_needs_load(int i) {
 // GPC from S = I with U taken as zero (the linear part A, into sA); no output rows, no Qh S.
 template <bool BF16, int D, int NCT, int NS, bool MAP = false>
 __global__ void __launch_bounds__((scan_threads<BF16, D, NCT, NS>()))
-chunk_scan_kernel(const int32_t *__restrict__ cu, int N, int T, int H, int nchains, float scale,
+chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, float scale,
                   const float *s0, float *sN,  // may alias: each element is read before it is written
                   typename ChunkSmem<BF16, D>::TIO *__restrict__ o, const char *__restrict__ ws,
                   float *__restrict__ sA, Window win) {
@@ -1488,7 +1488,7 @@ template <bool BF16, int D, int NCT, int NS, bool MAP>
 static hipError_t launch_scan_nct(const FwdArgs &a, const Window &win, hipStream_t st, int nchains) {
     const long blocks = (long)((nchains + 7) / 8) * 8 * (D / 16 / NCT) * (MAP ? 2 : 1);
     return launch_kernel(chunk_scan_kernel<BF16, D, NCT, NS, MAP>, dim3((unsigned)blocks),
-                         dim3(scan_threads<BF16, D, NCT, NS>()), st, a.cu_seqlens, a.N, a.T, a.H, nchains, a.scale,
+                         dim3(scan_threads<BF16, D, NCT, NS>()), st, a.cu_seqlens, a.T, a.H, nchains, a.scale,
                          MAP ? nullptr : a.s0, a.sN, a.o, a.ws, MAP ? a.map_A : nullptr, win);
 }
 
