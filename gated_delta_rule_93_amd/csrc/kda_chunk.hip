@@ -24,10 +24,11 @@
 // per-channel bridge e^{G_mI - G_mJ} <= 1).  If some |G_i - G_m| exceeds 115 (log2 units) the
 // chunk takes an exact element-wise fallback instead.
 //
-// Precision (bf16 inputs).  The Gram operands, Tm, Aqk, S and Ud enter the MFMAs as hi + lo
-// bf16 pairs (about 16 significant bits); U is kept at 24 bits (see pack_u24); Kh^T enters the
-// state update as its bf16 plane plus the remainder in fp8 with a per-channel scale (see st_kh).
-// q, k, v are used as stored (exact).  The fp32 path uses fp32 MFMAs and fp32 U throughout.
+// Precision (bf16 inputs).  The Gram operands, Tm, S and Ud enter the MFMAs as hi + lo bf16
+// pairs (about 16 significant bits); U is kept at 24 bits (see pack_u24); Kh^T and Aqk enter the
+// state update and the read-out as their bf16 plane plus the remainder in fp8 with a scale per
+// channel or per token row (see split_bf16_fp8).  q, k, v are used as stored (exact).  The fp32
+// path uses fp32 MFMAs and fp32 U throughout.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -89,13 +90,14 @@ template <> struct Prec<false> {
 
 // ------------------------------------------------------------------ workspace layout
 // Per (chunk slot, head): W, Qh fragments [tt][kb]; Kh^T fragments [rt][kb2]; Aqk fragments
-// (6 lower ones); e^gamma [D] and, for bf16, the per-channel scale 2^-a of the Kh^T low plane
-// [D] (together padded to 1 KB); U as accumulator tiles [jt][tt][lane] (f32x4; for bf16 the four
-// values as 24-bit floats in three dwords, see pack_u24); for bf16, the low
-// part of Kh^T [rt][kb2] (Kh^T minus its bf16 plane above) as fp8 e4m3 scaled by 2^a per
-// channel, 8 bytes per lane.  Everything before U is read by every column tile of the chain and
-// is staged in LDS by the state scan; U tile jt is read by column tile jt, the Kh^T low plane by
-// each wave for its own state rows.
+// (6 lower ones; for bf16 the bf16 plane, then the low part in fp8 e4m3, 8 bytes per lane and
+// fragment, scaled by 2^a per row, see split_bf16_fp8); e^gamma [D] and, for bf16, the scales 2^-a
+// of the Kh^T low plane [D] and of the Aqk low plane [64] as bf16 (together padded to 1 KB); U as
+// accumulator tiles [jt][tt][lane] (f32x4; for bf16 the four values as 24-bit floats in three
+// dwords, see pack_u24); for bf16, the low part of Kh^T [rt][kb2] (Kh^T minus its bf16 plane
+// above) as fp8 e4m3 scaled by 2^a per channel, 8 bytes per lane.  Everything before U is read by
+// every column tile of the chain and is staged in LDS by the state scan; U tile jt is read by
+// column tile jt, the Kh^T low plane by each wave for its own state rows.
 template <bool BF16, int D> struct WsLayout {
     static constexpr int NT = 4;           // 16-token tiles per chunk
     static constexpr int NKB = D / 32;     // 32-channel k-blocks
@@ -106,56 +108,78 @@ template <bool BF16, int D> struct WsLayout {
     static constexpr size_t offQ = offW + (size_t)nW * PP * 1024;
     static constexpr size_t offK = offQ + (size_t)nQ * PP * 1024;
     static constexpr size_t offA = offK + (size_t)nK * PP * 1024;
-    static constexpr size_t offE = offA + (size_t)nA * SP * 1024;
+    static constexpr size_t offAl = offA + (size_t)nA * 1024;  // Aqk low plane (bf16)
+    static constexpr size_t offE = offA + (size_t)nA * (BF16 ? 1024 + 512 : SP * 1024);
     static constexpr size_t offU = offE + 1024;
-    static constexpr size_t offEl = offE + (size_t)D * 4;  // scales of the Kh^T low plane (bf16)
+    static constexpr size_t offEl = offE + (size_t)D * 4;   // scales of the Kh^T low plane (bf16)
+    static constexpr size_t offEa = offEl + (size_t)D * 2;  // scales of the Aqk low plane (bf16)
     static constexpr size_t uTile = BF16 ? 768 : 1024;   // bytes of one U accumulator tile
     static constexpr size_t offKl = offU + (size_t)NRT * NT * uTile;
     static constexpr size_t bytes = offKl + (BF16 ? (size_t)nK * 512 : 0);
-    static_assert(D * 8 <= 1024, "e^gamma and the low-plane scales fit their 1 KB slot");
+    static_assert(D * 6 + kChunk * 2 <= 1024, "e^gamma and the low-plane scales fit their 1 KB slot");
 };
 
+// The bf16 plane of nf fragments (8 values per lane each) and the remainder lo = x - bf16(x) in
+// fp8 e4m3, scaled by 2^a, where a is shared by the lanes r16 + 16 g (one row of an A operand: a
+// channel of Kh^T, a token of Aqk) and chosen so that the largest |lo| of those lanes' fragments
+// lands in [64, 128), within the e4m3 range whichever e4m3 variant the hardware uses.  Returns the
+// scale 2^-a by which a product with the fp8 plane is multiplied back.  A product then takes x as
+// bf16 plane x (the other operand's hi + lo) plus fp8 plane x (the other operand in bf8): a single
+// bf16 rounding puts a relative error of 2^-9 on every term, the two planes about 2^-13.
+template <int NF>
+__device__ __forceinline__ float split_bf16_fp8(const float (&x)[NF][8], uint4 (&hi)[NF], uint2 (&lo8)[NF]) {
+    float lo[NF][8], m = 0.f;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        uint32_t hw[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t h = pk_bf16(x[f][2 * p], x[f][2 * p + 1]);
+            hw[p] = h;
+            lo[f][2 * p] = x[f][2 * p] - __uint_as_float(h << 16);
+            lo[f][2 * p + 1] = x[f][2 * p + 1] - __uint_as_float(h & 0xffff0000u);
+            m = fmaxf(m, fmaxf(fabsf(lo[f][2 * p]), fabsf(lo[f][2 * p + 1])));
+        }
+        hi[f] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    }
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    // a = 6 - floor(log2 m), within [-126, 126] (m = 0 or tiny: the low part is zero or negligible)
+    const int em = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
+    const int a = m > 0.f ? min(126, max(-126, 6 - em)) : 0;
+    const float up = __uint_as_float((uint32_t)(a + 127) << 23);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[f][0] * up, lo[f][1] * up, 0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[f][2] * up, lo[f][3] * up, w0, true);
+        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[f][4] * up, lo[f][5] * up, 0, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[f][6] * up, lo[f][7] * up, w1, true);
+        lo8[f] = make_uint2((uint32_t)w0, (uint32_t)w1);
+    }
+    return __uint_as_float((uint32_t)(127 - a) << 23);
+}
+// a power of two (or any value whose low 16 bits are zero) as bf16 bits
+__device__ __forceinline__ uint16_t bf16_exact(float x) { return (uint16_t)(__float_as_uint(x) >> 16); }
+
 // The two Kh^T fragments (row tile rt, token k-blocks 0 and 1) of a record.  fp32: as they are.
-// bf16: the bf16 plane (round to nearest even) and the low part lo = Kh - bf16(Kh) in fp8 e4m3,
-// scaled per channel by 2^a so that the channel's largest |lo| over the chunk's 64 tokens lands in
-// [64, 128) (within the e4m3 range whichever e4m3 variant the hardware uses); 2^-a goes to the
-// record for the state scan.  The state update takes Kh^T as bf16 plane x Ud (hi + lo) plus
-// low part x Ud in bf8: Kh^T single-rounded to bf16 puts a relative error of 2^-9 on every term
-// of Kh^T Ud, which the state carries; with the low part it is about 2^-13.  A channel's 64
-// tokens sit in this lane's two fragments and in the lanes r16 + 16 g of the other lane groups.
+// bf16: the bf16 plane and the fp8 low plane of split_bf16_fp8 with one scale per channel; the
+// state update takes Kh^T as bf16 plane x Ud (hi + lo) plus low plane x Ud in bf8 (Kh^T
+// single-rounded to bf16 puts a relative error of 2^-9 on every term of Kh^T Ud, which the
+// state carries from chunk to chunk).  A channel's 64 tokens sit in this lane's two fragments and
+// in the lanes r16 + 16 g of the other lane groups.
 template <bool BF16, int D>
 __device__ __forceinline__ void st_kh(char *wsb, int rt, int lane, const float (&kh)[2][8]) {
     using L = WsLayout<BF16, D>;
     if constexpr (BF16) {
-        float lo[2][8], m = 0.f;
+        uint4 hi[2];
+        uint2 lo8[2];
+        const float down = split_bf16_fp8<2>(kh, hi, lo8);
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-            uint32_t hw[4];
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const uint32_t h = pk_bf16(kh[kb2][2 * p], kh[kb2][2 * p + 1]);
-                hw[p] = h;
-                lo[kb2][2 * p] = kh[kb2][2 * p] - __uint_as_float(h << 16);
-                lo[kb2][2 * p + 1] = kh[kb2][2 * p + 1] - __uint_as_float(h & 0xffff0000u);
-                m = fmaxf(m, fmaxf(fabsf(lo[kb2][2 * p]), fabsf(lo[kb2][2 * p + 1])));
-            }
-            reinterpret_cast<uint4 *>(wsb + L::offK)[(rt * 2 + kb2) * 64 + lane] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+            reinterpret_cast<uint4 *>(wsb + L::offK)[(rt * 2 + kb2) * 64 + lane] = hi[kb2];
+            reinterpret_cast<uint2 *>(wsb + L::offKl)[(rt * 2 + kb2) * 64 + lane] = lo8[kb2];
         }
-        m = fmaxf(m, __shfl_xor(m, 16));
-        m = fmaxf(m, __shfl_xor(m, 32));
-        // a = 6 - floor(log2 m), within [-126, 126] (m = 0 or tiny: the low part is zero or negligible)
-        const int em = (int)((__float_as_uint(m) >> 23) & 0xffu) - 127;
-        const int a = m > 0.f ? min(126, max(-126, 6 - em)) : 0;
-        const float up = __uint_as_float((uint32_t)(a + 127) << 23), down = __uint_as_float((uint32_t)(127 - a) << 23);
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-            int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][0] * up, lo[kb2][1] * up, 0, false);
-            w0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][2] * up, lo[kb2][3] * up, w0, true);
-            int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][4] * up, lo[kb2][5] * up, 0, false);
-            w1 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[kb2][6] * up, lo[kb2][7] * up, w1, true);
-            reinterpret_cast<uint2 *>(wsb + L::offKl)[(rt * 2 + kb2) * 64 + lane] = make_uint2((uint32_t)w0, (uint32_t)w1);
-        }
-        if (lane < 16) reinterpret_cast<float *>(wsb + L::offEl)[16 * rt + lane] = down;
+        if (lane < 16) reinterpret_cast<uint16_t *>(wsb + L::offEl)[16 * rt + lane] = bf16_exact(down);
     } else {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) Prec<false>::st_plain(wsb + L::offK, L::nK, rt * 2 + kb2, lane, make_fragF(kh[kb2]));
@@ -371,15 +395,42 @@ __device__ __forceinline__ void ut_and_outputs(SM &sm, const Raw4<typename SM::T
 
     // ---------------- phase 5: Aqk fragments; then V^T into the dead Akk/Aqk region;
     // W = T' X and U = T' V.
-    for (int f = wave; f < 6; f += 4) {  // Aqk fragments
-        const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
-        const int t = 16 * tt + r16;
-        float vals[8];
-        ld_kslots(&sm.kq.a.Aqk[t][0], kb2, grp, vals);
+    if constexpr (BF16) {  // Aqk fragments of token tile `wave` (token k-blocks 0 .. wave / 2)
+        const int tt = wave, t = 16 * tt + r16;
+        float vals[2][8];
 #pragma unroll
-        for (int s = 0; s < 8; ++s)  // causal mask, incl. the diagonal (entries above were never written)
-            if (32 * kb2 + kslot(grp, s) > t) vals[s] = 0.f;
-        P::st_split(wsA, L::nA, f, lane, P::split(vals));
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+            if (kb2 <= tt / 2) {
+                ld_kslots(&sm.kq.a.Aqk[t][0], kb2, grp, vals[kb2]);
+#pragma unroll
+                for (int s = 0; s < 8; ++s)  // causal mask, incl. the diagonal (entries above were never written)
+                    if (32 * kb2 + kslot(grp, s) > t) vals[kb2][s] = 0.f;
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) vals[kb2][s] = 0.f;
+            }
+        }
+        uint4 hi[2];
+        uint2 lo8[2];
+        const float down = split_bf16_fp8<2>(vals, hi, lo8);  // one scale per token row
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+            if (kb2 <= tt / 2) {
+                reinterpret_cast<uint4 *>(wsA)[aidx(tt, kb2) * 64 + lane] = hi[kb2];
+                reinterpret_cast<uint2 *>(wsb + L::offAl)[aidx(tt, kb2) * 64 + lane] = lo8[kb2];
+            }
+        if (lane < 16) reinterpret_cast<uint16_t *>(wsb + L::offEa)[t] = bf16_exact(down);
+    } else {
+        for (int f = wave; f < 6; f += 4) {  // Aqk fragments
+            const int tt = f < 2 ? f : 2 + (f - 2) / 2, kb2 = f < 2 ? 0 : (f - 2) % 2;
+            const int t = 16 * tt + r16;
+            float vals[8];
+            ld_kslots(&sm.kq.a.Aqk[t][0], kb2, grp, vals);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)  // causal mask, incl. the diagonal (entries above were never written)
+                if (32 * kb2 + kslot(grp, s) > t) vals[s] = 0.f;
+            P::st_split(wsA, L::nA, f, lane, P::split(vals));
+        }
     }
     __syncthreads();  // Akk, Aqk are dead from here on
 #pragma unroll
@@ -1303,20 +1354,34 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
                 for (int kb2 = 0; kb2 < 2; ++kb2) kf[r][kb2] = ldK(r, kb2);
         }
         // Aqk fragments of the own output tiles: one k-block for tiles 0 and 1, two for 2 and 3
-        Split af[NOT][2];
+        // (fp32: both planes; bf16: the bf16 plane, the fp8 low plane and the low plane's scales
+        // for the tile's output rows 4 grp .. 4 grp + 3)
+        Split af[BF16 ? 1 : NOT][2];
+        Plain ah[BF16 ? NOT : 1][2];
+        long al[BF16 ? NOT : 1][2];
+        f32x4 asc[BF16 ? NOT : 1];
         if constexpr (!MAP) {
 #pragma unroll
             for (int i = 0; i < NOT; ++i) {
                 const int ot = own_tile(i);
-                af[i][0] = P::ld_split(sb + L::offA, L::nA, aidx(ot, 0), lane);
-                af[i][1] = P::ld_split(sb + L::offA, L::nA, aidx(ot, ot >= 2 ? 1 : 0), lane);
+                const int f0 = aidx(ot, 0), f1 = aidx(ot, ot >= 2 ? 1 : 0);
+                if constexpr (BF16) {
+                    ah[i][0] = P::ld_plain(sb + L::offA, L::nA, f0, lane);
+                    ah[i][1] = P::ld_plain(sb + L::offA, L::nA, f1, lane);
+                    al[i][0] = reinterpret_cast<const long *>(sb + L::offAl)[f0 * 64 + lane];
+                    al[i][1] = reinterpret_cast<const long *>(sb + L::offAl)[f1 * 64 + lane];
+                    asc[i] = load4(reinterpret_cast<const uint16_t *>(sb + L::offEa) + 16 * ot + 4 * grp);
+                } else {
+                    af[i][0] = P::ld_split(sb + L::offA, L::nA, f0, lane);
+                    af[i][1] = P::ld_split(sb + L::offA, L::nA, f1, lane);
+                }
             }
         }
         f32x4 e_cur[RTH], e_lo[BF16 ? RTH : 1];
 #pragma unroll
         for (int r = 0; r < RTH; ++r) {
             e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (part * RTH + r) + 4 * grp));
-            if constexpr (BF16) e_lo[r] = *reinterpret_cast<const f32x4 *>(sb + L::offEl + 4 * (16 * (part * RTH + r) + 4 * grp));
+            if constexpr (BF16) e_lo[r] = load4(reinterpret_cast<const uint16_t *>(sb + L::offEl) + 16 * (part * RTH + r) + 4 * grp);
         }
         // rows of the previous chunk (left in obuf before the top barrier; refilled after the
         // exchange barrier)
@@ -1343,7 +1408,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
                 for (int kb2 = 0; kb2 < 2; ++kb2) kl[r][kb2] = klx[((part * RTH + r) * 2 + kb2) * 64 + lane];
         }
         if constexpr (BF16) {
-            // the Kh^T low plane times Ud in bf8, scaled back per state row
+            // the Kh^T and Aqk low planes times Ud in bf8, scaled back per state row / output row
             long u8[2];
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2) u8[kb2] = *reinterpret_cast<const long *>(&ux[ct][0] + 4096 + (kb2 * 64 + lane) * 8);
@@ -1354,9 +1419,22 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
 #pragma unroll
                 for (int e = 0; e < 4; ++e) Sn[r][e] = fmaf(a8[e], e_lo[r][e], Sn[r][e]);
             }
-        }
 #pragma unroll
-        for (int i = 0; i < (MAP ? 0 : NOT); ++i) oo[i] = mfma(af[i][0], Uop[0], oo[i]);
+            for (int i = 0; i < (MAP ? 0 : NOT); ++i) {
+                f32x4 a8 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_bf8(al[i][0], u8[0], zero4(), 0, 0, 0);
+                if (own_tile(i) >= 2) a8 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_bf8(al[i][1], u8[1], a8, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oo[i][e] = fmaf(a8[e], asc[i][e], oo[i][e]);
+            }
+        }
+        // Aqk as the read-out takes it: its bf16 plane (the low plane was added above), both fp32
+        // planes otherwise
+        auto aop = [&](int i, int kb2) __attribute__((always_inline)) {
+            if constexpr (BF16) return ah[i][kb2];
+            else return af[i][kb2];
+        };
+#pragma unroll
+        for (int i = 0; i < (MAP ? 0 : NOT); ++i) oo[i] = mfma(aop(i, 0), Uop[0], oo[i]);
         // Kh^T as the state update takes it: its bf16 plane (the low plane was added above), fp32
         // as stored otherwise
         auto khop = [&](int r, int kb2) __attribute__((always_inline)) {
@@ -1366,7 +1444,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
         for (int r = 0; r < RTH; ++r) Sn[r] = mfma(khop(r, 0), Uop[0], Sn[r]);
 #pragma unroll
         for (int i = 0; i < (MAP ? 0 : NOT); ++i)
-            if (own_tile(i) >= 2) oo[i] = mfma(af[i][1], Uop[1], oo[i]);
+            if (own_tile(i) >= 2) oo[i] = mfma(aop(i, 1), Uop[1], oo[i]);
 #pragma unroll
         for (int r = 0; r < RTH; ++r) S[r] = mfma(khop(r, 1), Uop[1], Sn[r]);
         // every read of sx for this chunk was complete at the exchange barrier

@@ -63,8 +63,8 @@ const char *kda_status_string(kda_status_t status);
 /*
  * Workspace for kda_fwd to run every chunk in one pass (bytes, a multiple of 256); the two phases
  * kda_fwd_chunk_local / kda_fwd_state_scan and kda_fwd_segment_map always need this much.
- * It is one record per (chunk, head): 95,232 bytes at d = 128 in bf16 (1,488 bytes per
- * token-head), i.e. it grows with T * H (about 390 MB for 4 x 4096 tokens x 16 heads, 6.2 GB for
+ * It is one record per (chunk, head): 92,160 bytes at d = 128 in bf16 (1,440 bytes per
+ * token-head), i.e. it grows with T * H (about 377 MB for 4 x 4096 tokens x 16 heads, 6.0 GB for
  * 131,072 tokens x 32 heads).  A packed batch has N extra chunk slots (sequences need not start
  * on a chunk boundary).
  * varlen != 0 means cu_seqlens will be passed; then B must be 1 and T is the packed
