@@ -666,7 +666,9 @@ def measured_mfma(workload, kernel):
 #   rocprofv3 --kernel-trace --stats -f csv -d DIR/<leg>/trace -o trace -- python3 bench.py --only <leg>,copy --steps 5 --warmup 2
 #   rocprofv3 --pmc FETCH_SIZE       -f csv -d DIR/<leg>/fetch -o fetch -- python3 bench.py --only <leg>,copy --steps 5 --warmup 2
 #   rocprofv3 --pmc WRITE_SIZE       -f csv -d DIR/<leg>/write -o write -- python3 bench.py --only <leg>,copy --steps 5 --warmup 2
-# and optionally DIR/<leg>/mfma (--pmc MfmaUtil MfmaFlopsBF16).  The copy leg runs a 256 MiB
+# and optionally DIR/<leg>/mfma (--pmc MfmaUtil MfmaFlopsBF16) and DIR/<leg>/insts (--pmc with the
+# INSTS_COUNTERS below: instructions issued per wave, and the share of wave cycles spent waiting to
+# issue LDS instructions).  The copy leg runs a 256 MiB
 # device copy in the same process: its FETCH_SIZE / WRITE_SIZE (KiB) against the 268,435,456 bytes
 # it reads and writes give the scale factors applied to every kernel of the leg.
 def _short_kernel(name):
@@ -696,6 +698,8 @@ def _counters(path):
 
 
 PROFILE_STEPS = "--steps 5 --warmup 2"
+INSTS_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM SQ_WAIT_INST_LDS "
+                  "SQ_WAVE_CYCLES")
 
 
 def summarize_profiles(top, cmd_prefix="rocprofv3"):
@@ -713,6 +717,7 @@ def summarize_profiles(top, cmd_prefix="rocprofv3"):
               f"{cmd_prefix} --pmc FETCH_SIZE -f csv -d <out>/{leg}/fetch -o fetch -- python3 <repo>/bench.py --only {leg},copy {PROFILE_STEPS}",
               f"{cmd_prefix} --pmc WRITE_SIZE -f csv -d <out>/{leg}/write -o write -- python3 <repo>/bench.py --only {leg},copy {PROFILE_STEPS}",
               f"{cmd_prefix} --pmc MfmaUtil MfmaFlopsBF16 -f csv -d <out>/{leg}/mfma -o mfma -- python3 <repo>/bench.py --only {leg} {PROFILE_STEPS}   (prefill, long, varlen)",
+              f"{cmd_prefix} --pmc {INSTS_COUNTERS} -f csv -d <out>/{leg}/insts -o insts -- python3 <repo>/bench.py --only {leg} {PROFILE_STEPS}   (prefill, long, varlen)",
               f"python3 <repo>/bench.py --summarize <out>", "```", ""]
         stats = _find_csv(os.path.join(d, "trace"), "kernel_stats.csv")
         if stats:
@@ -760,6 +765,26 @@ def summarize_profiles(top, cmd_prefix="rocprofv3"):
                     entry["mfma"][k] = {"util_pct": sum(u) / len(u), "bf16_flops_issued": sum(fl) / len(fl)}
                     md.append(f"| `{k}` | {len(u)} | {sum(u) / len(u):.1f} | {sum(fl) / len(fl) / 1e9:.2f} |")
             md.append("")
+        ipath = _find_csv(os.path.join(d, "insts"), "counter_collection.csv")
+        if ipath:
+            ic = _counters(ipath)
+            md += ["Instructions issued per wave (SQ_INSTS_* / SQ_WAVES, averaged over launches) and the share of "
+                   "wave cycles spent waiting to issue an LDS instruction (SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES, both in "
+                   "units of 4 cycles):", "",
+                   "| kernel | launches | waves | VALU | MFMA | LDS | SALU | VMEM | LDS issue wait (%) |",
+                   "|---|---|---|---|---|---|---|---|---|"]
+            entry["insts"] = {}
+            for k, c in sorted(ic.items()):
+                if k == copy_name or not c.get("SQ_WAVES"):
+                    continue
+                mean = {n: sum(v) / len(v) for n, v in c.items()}
+                w = mean["SQ_WAVES"]
+                per = {n: mean.get(f"SQ_INSTS_{n}", 0.0) / w for n in ("VALU", "MFMA", "LDS", "SALU", "VMEM")}
+                wait = 100.0 * mean.get("SQ_WAIT_INST_LDS", 0.0) / max(mean.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+                entry["insts"][k] = dict(waves=w, lds_issue_wait_pct=wait, **{f"{n.lower()}_per_wave": x for n, x in per.items()})
+                md.append(f"| `{k}` | {len(c['SQ_WAVES'])} | {w:.0f} | {per['VALU']:.0f} | {per['MFMA']:.0f} | "
+                          f"{per['LDS']:.0f} | {per['SALU']:.0f} | {per['VMEM']:.0f} | {wait:.1f} |")
+            md.append("")
         table["workloads"][leg] = entry
         with open(os.path.join(ROOT, "profiles", f"kda_{leg}_rocprof_summary.md"), "w") as fh:
             fh.write("\n".join(md))
@@ -797,7 +822,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write profiles/traffic.json and profiles/kda_<leg>_rocprof_summary.md from rocprofv3 "
-                         "csv output under DIR/<leg>/{trace,fetch,write,mfma} (no GPU needed)")
+                         "csv output under DIR/<leg>/{trace,fetch,write,mfma,insts} (no GPU needed)")
     ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,attnres,long,kcp,varlen,cpu",
                     help="comma list of prefill, decode, prep, scalar, gate, attnres, long, kcp, varlen, cpu, "
                          "copy")
