@@ -92,7 +92,8 @@ template <> struct Prec<false> {
 // Per (chunk slot, head): W, Qh fragments [tt][kb]; Kh^T fragments [rt][kb2]; Aqk fragments
 // (6 lower ones; for bf16 the bf16 plane, then the low part in fp8 e4m3, 8 bytes per lane and
 // fragment, scaled by 2^a per row, see split_bf16_fp8); e^gamma [D] and, for bf16, the scales 2^-a
-// of the Kh^T low plane [D] and of the Aqk low plane [64] as bf16 (together padded to 1 KB); U as
+// of the Kh^T low plane [D] and of the Aqk low plane [64] as bf16 and the exponents of the bf8 scale
+// of Ud per value column [D] as int8 (see ut_and_outputs; together padded to 1 KB); U as
 // accumulator tiles [jt][tt][lane] (f32x4; for bf16 the four values as 24-bit floats in three
 // dwords, see pack_u24); for bf16, the low part of Kh^T [rt][kb2] (Kh^T minus its bf16 plane
 // above) as fp8 e4m3 scaled by 2^a per channel, 8 bytes per lane.  Everything before U is read by
@@ -113,10 +114,11 @@ template <bool BF16, int D> struct WsLayout {
     static constexpr size_t offU = offE + 1024;
     static constexpr size_t offEl = offE + (size_t)D * 4;   // scales of the Kh^T low plane (bf16)
     static constexpr size_t offEa = offEl + (size_t)D * 2;  // scales of the Aqk low plane (bf16)
+    static constexpr size_t offEs = offEa + (size_t)kChunk * 2;  // bf8 scale exponents of Ud's columns (bf16)
     static constexpr size_t uTile = BF16 ? 768 : 1024;   // bytes of one U accumulator tile
     static constexpr size_t offKl = offU + (size_t)NRT * NT * uTile;
     static constexpr size_t bytes = offKl + (BF16 ? (size_t)nK * 512 : 0);
-    static_assert(D * 6 + kChunk * 2 <= 1024, "e^gamma and the low-plane scales fit their 1 KB slot");
+    static_assert(D * 7 + kChunk * 2 <= 1024, "e^gamma and the low-plane scales fit their 1 KB slot");
 };
 
 // The bf16 plane of nf fragments (8 values per lane each) and the remainder lo = x - bf16(x) in
@@ -473,6 +475,10 @@ __device__ __forceinline__ void ut_and_outputs(SM &sm, const Raw4<typename SM::T
             P::st_plain(wsW, L::nW, tt * NKB + kb, lane, P::plain(vals));
         }
     }
+    // bf16: for each value column, the exponent s that brings the chunk's largest |U| in the column
+    // into [1, 2).  The state scan forms Ud in bf8 (for the fp8 low planes of Kh^T and Aqk) as
+    // bf8(Ud 2^s) and scales the products back by 2^-s, so that Ud's bf8 form stays inside bf8's
+    // normal range whatever the magnitude of v (Ud = U - W S is of U's order).
     for (int jt = wave; jt < NRT; jt += 4) {  // U tiles (jt, tt)
         Plain Vf[2];
 #pragma unroll
@@ -481,13 +487,25 @@ __device__ __forceinline__ void ut_and_outputs(SM &sm, const Raw4<typename SM::T
             ld_kslots(&sm.kq.VT[16 * jt + r16][0], kb2, grp, vals);
             Vf[kb2] = P::plain(vals);
         }
+        float um = 0.f;  // largest |U| of this lane's column (r16) over its rows
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kb2 = 0; kb2 <= tt / 2; ++kb2) acc = mfma(Tf[aidx(tt, kb2)], Vf[kb2], acc);
-            if constexpr (BF16) reinterpret_cast<U24 *>(wsb + L::offU)[(jt * 4 + tt) * 64 + lane] = pack_u24(acc);
-            else reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
+            if constexpr (BF16) {
+                reinterpret_cast<U24 *>(wsb + L::offU)[(jt * 4 + tt) * 64 + lane] = pack_u24(acc);
+                um = fmaxf(um, fmaxf(fmaxf(fabsf(acc[0]), fabsf(acc[1])), fmaxf(fabsf(acc[2]), fabsf(acc[3]))));
+            } else {
+                reinterpret_cast<f32x4 *>(wsU)[(jt * 4 + tt) * 64 + lane] = acc;
+            }
+        }
+        if constexpr (BF16) {
+            um = fmaxf(um, __shfl_xor(um, 16));
+            um = fmaxf(um, __shfl_xor(um, 32));
+            const int eu = (int)((__float_as_uint(um) >> 23) & 0xffu) - 127;  // floor(log2 um), normal um
+            const int su = um > 0.f ? min(126, max(-126, -eu)) : 0;
+            if (lane < 16) reinterpret_cast<int8_t *>(wsb + L::offEs)[16 * jt + lane] = (int8_t)su;
         }
     }
 }
@@ -1273,6 +1291,15 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
         __syncthreads();                // ... and every copy: chunk c is in LDS, and so is the state
         const bool more = c + 1 < nck;
         const char *sb = buf ? stage1 : stage0;
+        // bf16: 2^s for this lane's value column, under which Ud takes its bf8 form (see
+        // ut_and_outputs), and 2^-s; the linear part of a segment map (U taken as zero, from S = I)
+        // keeps s = 0
+        float usc = 1.f, uinv = 1.f;
+        if constexpr (BF16) {
+            const int su = amap ? 0 : (int)reinterpret_cast<const int8_t *>(sb + L::offEs)[col];
+            usc = __uint_as_float((uint32_t)(127 + su) << 23);
+            uinv = __uint_as_float((uint32_t)(127 - su) << 23);
+        }
         // the state (every k-block) and the W and Qh fragments of the own token tiles; bf16 ones are
         // all requested before the first product (fp32 ones take twice the registers and are read
         // next to their use)
@@ -1330,10 +1357,10 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
                 const uint32_t l23 = pk_bf16(ud[2] - __uint_as_float(h23 << 16), ud[3] - __uint_as_float(h23 & 0xffff0000u));
                 *reinterpret_cast<uint2 *>(dst + (ot & 1) * 8) = make_uint2(h01, h23);
                 *reinterpret_cast<uint2 *>(dst + 2048 + (ot & 1) * 8) = make_uint2(l01, l23);
-                // bf8 (clamped to its largest finite value) for the Kh^T low plane
+                // bf8 of Ud 2^s (clamped to its largest finite value) for the low planes of Kh^T and Aqk
                 float c8[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) c8[e] = fminf(fmaxf(ud[e], -57344.f), 57344.f);
+                for (int e = 0; e < 4; ++e) c8[e] = fminf(fmaxf(ud[e] * usc, -57344.f), 57344.f);
                 int w8 = __builtin_amdgcn_cvt_pk_bf8_f32(c8[0], c8[1], 0, false);
                 w8 = __builtin_amdgcn_cvt_pk_bf8_f32(c8[2], c8[3], w8, true);
                 *reinterpret_cast<int *>(&ux[ct][0] + 4096 + ((ot >> 1) * 64 + lane) * 8 + (ot & 1) * 4) = w8;
@@ -1382,6 +1409,12 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
         for (int r = 0; r < RTH; ++r) {
             e_cur[r] = *reinterpret_cast<const f32x4 *>(sb + L::offE + 4 * (16 * (part * RTH + r) + 4 * grp));
             if constexpr (BF16) e_lo[r] = load4(reinterpret_cast<const uint16_t *>(sb + L::offEl) + 16 * (part * RTH + r) + 4 * grp);
+        }
+        if constexpr (BF16) {  // the products with Ud's bf8 form are scaled back by 2^-s
+#pragma unroll
+            for (int r = 0; r < RTH; ++r) e_lo[r] *= uinv;
+#pragma unroll
+            for (int i = 0; i < (MAP ? 0 : NOT); ++i) asc[i] *= uinv;
         }
         // rows of the previous chunk (left in obuf before the top barrier; refilled after the
         // exchange barrier)

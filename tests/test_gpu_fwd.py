@@ -77,6 +77,26 @@ def test_fwd_two_tile_scan_shapes(io, d, B, H):
                   label=f"two-tile scan {io} d={d} chains={B * H}")
 
 
+def test_fwd_value_scale_equivariance():
+    """v and S_0 scaled by 2^e (exact in bf16; q, k unit-norm as the method assumes): o and the
+    final state scale by 2^e bit for bit, since every rounding on the path (the bf16 splits, U in
+    24 bits, Ud's bf8 form under its per-column power-of-two scale) commutes with a power-of-two
+    scaling of the values.  With e = 14 U and Ud reach ~10^5, beyond bf8's largest value (57,344);
+    with e = -20 they lie below bf8's normal range: unscaled, the fp8 correction terms of Kh^T and
+    Aqk would clamp or lose them.  The unscaled run is checked against the oracle."""
+    base = ki.make_dense(1, 300, 3, 128, 128, "bf16", 23, s0_std=0.1, g_shift=-5.0)
+    o0, S0 = run_and_check(base, label="v, S0 as drawn")
+    for e in (14, -20):
+        inp = ki.make_dense(1, 300, 3, 128, 128, "bf16", 23, s0_std=0.1, g_shift=-5.0)
+        inp.v *= np.float32(2.0 ** e)
+        inp.S0 *= np.float32(2.0 ** e)
+        q, k, v, g, beta, S_in, _ = upload(inp)
+        o, S = kda.fwd(q, k, v, g, beta, 1.0, S_in)
+        torch.cuda.synchronize()
+        assert torch.equal(o, (o0.float() * 2.0 ** e).to(o0.dtype)), e
+        assert torch.equal(S, S0 * 2.0 ** e), e
+
+
 @pytest.mark.parametrize("variant", ["weak_decay", "alpha_one", "scalar_alpha"])
 def test_fwd_long_memory_variants(variant):
     """Decay regimes that exercise state propagation across many chunks."""
