@@ -83,7 +83,8 @@ def test_fwd_value_scale_equivariance():
     24 bits, Ud's bf8 form under its per-column power-of-two scale) commutes with a power-of-two
     scaling of the values.  With e = 14 U and Ud reach ~10^5, beyond bf8's largest value (57,344);
     with e = -20 they lie below bf8's normal range: unscaled, the fp8 correction terms of Kh^T and
-    Aqk would clamp or lose them.  The unscaled run is checked against the oracle."""
+    Aqk would clamp or lose them.  q scaled by 2^-12 scales o alone.  The unscaled run is checked
+    against the oracle."""
     base = ki.make_dense(1, 300, 3, 128, 128, "bf16", 23, s0_std=0.1, g_shift=-5.0)
     o0, S0 = run_and_check(base, label="v, S0 as drawn")
     for e in (14, -20):
@@ -95,6 +96,14 @@ def test_fwd_value_scale_equivariance():
         torch.cuda.synchronize()
         assert torch.equal(o, (o0.float() * 2.0 ** e).to(o0.dtype)), e
         assert torch.equal(S, S0 * 2.0 ** e), e
+    # q enters o linearly and the state not at all (the Aqk low plane's row scales follow it)
+    inp = ki.make_dense(1, 300, 3, 128, 128, "bf16", 23, s0_std=0.1, g_shift=-5.0)
+    inp.q *= np.float32(2.0 ** -12)
+    q, k, v, g, beta, S_in, _ = upload(inp)
+    o, S = kda.fwd(q, k, v, g, beta, 1.0, S_in)
+    torch.cuda.synchronize()
+    assert torch.equal(o, (o0.float() * 2.0 ** -12).to(o0.dtype))
+    assert torch.equal(S, S0)
 
 
 @pytest.mark.parametrize("variant", ["weak_decay", "alpha_one", "scalar_alpha"])
