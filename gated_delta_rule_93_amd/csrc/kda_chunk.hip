@@ -27,8 +27,9 @@
 // Precision (bf16 inputs).  The Gram operands, Tm, S and Ud enter the MFMAs as hi + lo bf16
 // pairs (about 16 significant bits); U is kept at 24 bits (see pack_u24); Kh^T and Aqk enter the
 // state update and the read-out as their bf16 plane plus the remainder in fp8 with a scale per
-// channel or per token row (see split_bf16_fp8).  q, k, v are used as stored (exact).  The fp32
-// path uses fp32 MFMAs and fp32 U throughout.
+// channel or per token row (see split_bf16_fp8), the remainder times Ud in bf8 under a
+// power-of-two scale per value column (see ut_and_outputs).  q, k, v are used as stored (exact).
+// The fp32 path uses fp32 MFMAs and fp32 U throughout.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
