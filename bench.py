@@ -659,6 +659,13 @@ def measured_mfma(workload, kernel):
     return None if t is None else t.get("workloads", {}).get(workload, {}).get("mfma", {}).get(kernel)
 
 
+def measured_insts(workload, kernel):
+    """rocprofv3 instructions issued per wave (VALU, MFMA, LDS, SALU, VMEM) and the share of wave
+    cycles spent waiting to issue LDS instructions, for `kernel` in leg `workload`."""
+    t = _traffic_table()
+    return None if t is None else t.get("workloads", {}).get(workload, {}).get("insts", {}).get(kernel)
+
+
 # ----------------------------------------------------------------------------- profile summaries
 # `python bench.py --summarize DIR` turns rocprofv3 csv output into profiles/traffic.json and the
 # text summaries under profiles/.  DIR/<leg>/ holds the output of three runs of one bench leg
@@ -810,7 +817,8 @@ def roofline_block(leg, th, ms_whole, kernels):
     whole["frac"] = whole["achieved"] / HBM_PEAK_GBS
     tr = {k: measured_traffic(leg, name) for k, (name, _) in kernels.items()}
     whole["traffic"] = None if any(v is None for v in tr.values()) else sum(tr.values())
-    per_kernel = {k: {"kernel": name, "ms": ms, "traffic": tr[k], "mfma": measured_mfma(leg, name)}
+    per_kernel = {k: {"kernel": name, "ms": ms, "traffic": tr[k], "mfma": measured_mfma(leg, name),
+                      "insts_per_wave": measured_insts(leg, name)}
                   for k, (name, ms) in kernels.items()}
     return r, whole, per_kernel
 
