@@ -77,31 +77,43 @@ def test_fwd_two_tile_scan_shapes(io, d, B, H):
                   label=f"two-tile scan {io} d={d} chains={B * H}")
 
 
-def test_fwd_value_scale_equivariance():
+@pytest.mark.parametrize("kind,d", [("channel", 128), ("channel", 64), ("scalar", 128)])
+def test_fwd_value_scale_equivariance(kind, d):
     """v and S_0 scaled by 2^e (exact in bf16; q, k unit-norm as the method assumes): o and the
     final state scale by 2^e bit for bit, since every rounding on the path (the bf16 splits, U in
     24 bits, Ud's bf8 form under its per-column power-of-two scale) commutes with a power-of-two
     scaling of the values.  With e = 14 U and Ud reach ~10^5, beyond bf8's largest value (57,344);
     with e = -20 they lie below bf8's normal range: unscaled, the fp8 correction terms of Kh^T and
-    Aqk would clamp or lose them.  q scaled by 2^-12 scales o alone.  The unscaled run is checked
+    Aqk would clamp or lose them.  q scaled by 2^-12 scales o alone.  Per-channel decay (kda_fwd)
+    at d = 128 and 64, and one decay per head (kda_fwd_scalar_gate); the unscaled run is checked
     against the oracle."""
-    base = ki.make_dense(1, 300, 3, 128, 128, "bf16", 23, s0_std=0.1, g_shift=-5.0)
-    o0, S0 = run_and_check(base, label="v, S0 as drawn")
-    for e in (14, -20):
-        inp = ki.make_dense(1, 300, 3, 128, 128, "bf16", 23, s0_std=0.1, g_shift=-5.0)
-        inp.v *= np.float32(2.0 ** e)
-        inp.S0 *= np.float32(2.0 ** e)
+    def inputs(ev=0, eq=0):
+        inp = ki.make_dense(1, 300, 3, d, d, "bf16", 23, s0_std=0.1, g_shift=-5.0)
+        if kind == "scalar":
+            inp.g[:] = inp.g[..., :1]
+        inp.v *= np.float32(2.0 ** ev)
+        inp.S0 *= np.float32(2.0 ** ev)
+        inp.q *= np.float32(2.0 ** eq)
+        return inp
+
+    def run(inp):
         q, k, v, g, beta, S_in, _ = upload(inp)
-        o, S = kda.fwd(q, k, v, g, beta, 1.0, S_in)
+        if kind == "scalar":
+            o, S = kda.fwd_scalar_gate(q, k, v, g[..., 0].contiguous(), beta, 1.0, S_in)
+        else:
+            o, S = kda.fwd(q, k, v, g, beta, 1.0, S_in)
         torch.cuda.synchronize()
+        return o, S
+
+    base = inputs()
+    o0, S0 = run(base)
+    check_against_oracle(base, o0, S0, label=f"{kind} d={d}, v and S0 as drawn")
+    for e in (14, -20):
+        o, S = run(inputs(ev=e))
         assert torch.equal(o, (o0.float() * 2.0 ** e).to(o0.dtype)), e
         assert torch.equal(S, S0 * 2.0 ** e), e
     # q enters o linearly and the state not at all (the Aqk low plane's row scales follow it)
-    inp = ki.make_dense(1, 300, 3, 128, 128, "bf16", 23, s0_std=0.1, g_shift=-5.0)
-    inp.q *= np.float32(2.0 ** -12)
-    q, k, v, g, beta, S_in, _ = upload(inp)
-    o, S = kda.fwd(q, k, v, g, beta, 1.0, S_in)
-    torch.cuda.synchronize()
+    o, S = run(inputs(eq=-12))
     assert torch.equal(o, (o0.float() * 2.0 ** -12).to(o0.dtype))
     assert torch.equal(S, S0)
 
