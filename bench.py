@@ -675,7 +675,8 @@ def measured_insts(workload, kernel):
 #   rocprofv3 --pmc WRITE_SIZE       -f csv -d DIR/<leg>/write -o write -- python3 bench.py --only <leg>,copy --steps 5 --warmup 2
 # and optionally DIR/<leg>/mfma (--pmc MfmaUtil MfmaFlopsBF16) and DIR/<leg>/insts (--pmc with the
 # INSTS_COUNTERS below: instructions issued per wave, and the share of wave cycles spent waiting to
-# issue LDS instructions).  The copy leg runs a 256 MiB
+# issue LDS instructions) and DIR/<leg>/stall (--pmc with the STALL_COUNTERS: where the waves' cycles
+# go).  The copy leg runs a 256 MiB
 # device copy in the same process: its FETCH_SIZE / WRITE_SIZE (KiB) against the 268,435,456 bytes
 # it reads and writes give the scale factors applied to every kernel of the leg.
 def _short_kernel(name):
@@ -707,6 +708,8 @@ def _counters(path):
 PROFILE_STEPS = "--steps 5 --warmup 2"
 INSTS_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_VMEM SQ_WAIT_INST_LDS "
                   "SQ_WAVE_CYCLES")
+STALL_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU "
+                  "SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA")
 
 
 def summarize_profiles(top, cmd_prefix="rocprofv3"):
@@ -725,6 +728,7 @@ def summarize_profiles(top, cmd_prefix="rocprofv3"):
               f"{cmd_prefix} --pmc WRITE_SIZE -f csv -d <out>/{leg}/write -o write -- python3 <repo>/bench.py --only {leg},copy {PROFILE_STEPS}",
               f"{cmd_prefix} --pmc MfmaUtil MfmaFlopsBF16 -f csv -d <out>/{leg}/mfma -o mfma -- python3 <repo>/bench.py --only {leg} {PROFILE_STEPS}   (prefill, long, varlen)",
               f"{cmd_prefix} --pmc {INSTS_COUNTERS} -f csv -d <out>/{leg}/insts -o insts -- python3 <repo>/bench.py --only {leg} {PROFILE_STEPS}   (prefill, long, varlen)",
+              f"{cmd_prefix} --pmc {STALL_COUNTERS} -f csv -d <out>/{leg}/stall -o stall -- python3 <repo>/bench.py --only {leg} {PROFILE_STEPS}   (prefill, long, varlen)",
               f"python3 <repo>/bench.py --summarize <out>", "```", ""]
         stats = _find_csv(os.path.join(d, "trace"), "kernel_stats.csv")
         if stats:
@@ -792,6 +796,30 @@ def summarize_profiles(top, cmd_prefix="rocprofv3"):
                 md.append(f"| `{k}` | {len(c['SQ_WAVES'])} | {w:.0f} | {per['VALU']:.0f} | {per['MFMA']:.0f} | "
                           f"{per['LDS']:.0f} | {per['SALU']:.0f} | {per['VMEM']:.0f} | {wait:.1f} |")
             md.append("")
+        spath = _find_csv(os.path.join(d, "stall"), "counter_collection.csv")
+        if spath:
+            sc = _counters(spath)
+            md += ["Where the waves' cycles go, as shares of SQ_WAVE_CYCLES (the cycles waves are resident; "
+                   "the wait counters count in the same 4-cycle units; the ACTIVE_INST counters are taken as "
+                   "reported, so their shares are indicative): waiting for anything (dependencies, "
+                   "`s_waitcnt`, barriers), waiting to issue, and working on any, vector ALU, vector memory, "
+                   "LDS and scalar instructions:", "",
+                   "| kernel | launches | wait any (%) | wait issue (%) | active any (%) | VALU (%) | VMEM (%) | LDS (%) | scalar (%) |",
+                   "|---|---|---|---|---|---|---|---|---|"]
+            entry["stall"] = {}
+            for k, c in sorted(sc.items()):
+                if k == copy_name or not c.get("SQ_WAVE_CYCLES"):
+                    continue
+                mean = {n: sum(v) / len(v) for n, v in c.items()}
+                wc = max(mean["SQ_WAVE_CYCLES"], 1.0)
+                sh = {n: 100.0 * mean.get(n, 0.0) / wc for n in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                                                                  "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM",
+                                                                  "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_SCA")}
+                entry["stall"][k] = {n.replace("SQ_", "").lower() + "_pct": x for n, x in sh.items()}
+                md.append(f"| `{k}` | {len(c['SQ_WAVE_CYCLES'])} | {sh['SQ_WAIT_ANY']:.1f} | {sh['SQ_WAIT_INST_ANY']:.1f} | "
+                          f"{sh['SQ_ACTIVE_INST_ANY']:.1f} | {sh['SQ_ACTIVE_INST_VALU']:.1f} | {sh['SQ_ACTIVE_INST_VMEM']:.1f} | "
+                          f"{sh['SQ_ACTIVE_INST_LDS']:.1f} | {sh['SQ_ACTIVE_INST_SCA']:.1f} |")
+            md.append("")
         table["workloads"][leg] = entry
         with open(os.path.join(ROOT, "profiles", f"kda_{leg}_rocprof_summary.md"), "w") as fh:
             fh.write("\n".join(md))
@@ -830,7 +858,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write profiles/traffic.json and profiles/kda_<leg>_rocprof_summary.md from rocprofv3 "
-                         "csv output under DIR/<leg>/{trace,fetch,write,mfma,insts} (no GPU needed)")
+                         "csv output under DIR/<leg>/{trace,fetch,write,mfma,insts,stall} (no GPU needed)")
     ap.add_argument("--only", default="prefill,decode,prep,scalar,gate,attnres,long,kcp,varlen,cpu",
                     help="comma list of prefill, decode, prep, scalar, gate, attnres, long, kcp, varlen, cpu, "
                          "copy")
