@@ -60,7 +60,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 template <int J>
 __global__ void __launch_bounds__(256) attnres_online_kernel(AttnResArgs a) {
     const int lane = threadIdx.x & 63;
-    const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long t = (long)blockIdx.x * 4 + wave_id();
     if (t >= a.T) return;  // whole wave
     const float inv_d = 1.f / (float)(512 * J);
     const long row = t * (512 * J) + 8 * lane;
@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(256) attnres_online_kernel(AttnResArgs a) {
 // with lane (grp, r16) holding the 8 consecutive width indices 32 kb + 8 grp .. (A and B alike).
 // A second MFMA of the tile with itself gives sum x^2 of each token row on its diagonal.
 __global__ void __launch_bounds__(256) attnres_scores_kernel(AttnScoreArgs a) {
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     const int b = blockIdx.y;
     const long t0 = ((long)blockIdx.x * 4 + wave) * 16;
     if (t0 >= a.T) return;  // whole wave
@@ -177,7 +177,7 @@ __global__ void __launch_bounds__(256) attnres_scores_kernel(AttnScoreArgs a) {
 template <int NB>
 __global__ void __launch_bounds__(256) attnres_mix_kernel(AttnMixArgs a) {
     __shared__ float wts[4][kAttnResMaxLayers][NB];  // [wave][layer][block]
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const long t = (long)blockIdx.x * 4 + wave;
     if (t >= a.T) return;  // whole wave; no workgroup barrier below
     const float inv_d = 1.f / (float)a.d;

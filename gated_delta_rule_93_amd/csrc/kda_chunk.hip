@@ -358,7 +358,7 @@ __device__ __forceinline__ void ut_and_outputs(SM &sm, const Raw4<typename SM::T
     using Plain = typename P::Plain;
     using Split = typename P::Split;
     constexpr int NKB = L::NKB, NRT = L::NRT;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     char *wsW = wsb + L::offW, *wsA = wsb + L::offA;
     float *wsU = reinterpret_cast<float *>(wsb + L::offU);
     // ---------------- phase 4: Tm = (I + Akk)^-1 (unit lower triangular), fp32
@@ -543,7 +543,7 @@ chunk_local_kernel(const typename ChunkSmem<BF16, D>::TIO *__restrict__ q,
     const ChunkPos pos = local_chunk(blockIdx.x, cu, N, T, H, win, rec, h);
     if (!pos.valid) return;  // uniform over the block
     const int Cc = pos.Cc;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     char *wsb = ws + ((size_t)rec * H + h) * L::bytes;
     const long rowstride = (long)H * D;  // elements between consecutive tokens
     const long base_in = (pos.tok0 * H + h) * (long)D;
@@ -885,7 +885,7 @@ chunk_local_scalar_kernel(const typename ChunkSmemS<BF16, D>::TIO *__restrict__ 
     const ChunkPos pos = local_chunk(blockIdx.x, cu, N, T, H, win, rec, h);
     if (!pos.valid) return;  // uniform over the block
     const int Cc = pos.Cc;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     char *wsb = ws + ((size_t)rec * H + h) * L::bytes;
     const long rowstride = (long)H * D;
     const long base_in = (pos.tok0 * H + h) * (long)D;
@@ -1105,7 +1105,7 @@ chunk_scan_kernel(const int32_t *__restrict__ cu, int T, int H, int nchains, flo
     const bool amap = MAP && jgm >= GPC;  // this workgroup forms columns of A
     const int jg = amap ? jgm - GPC : jgm;
     const int n = chain / H, h = chain % H;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
+    const int wave = wave_id(), lane = threadIdx.x & 63, grp = lane >> 4, r16 = lane & 15;
     const bool producer = kProd && wave >= NW;
     const int ct = producer ? 0 : wave / NS, part = wave % NS;
     const int jt = jg * NCT + ct;

@@ -51,7 +51,7 @@ __global__ void __launch_bounds__(512) gate_kernel(GateArgs a) {
         uint16_t w[2][2][4][16][136];
         float g[8][16][132];
     } stg;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     const int tt = wave & 3, kh = wave >> 2;
     const long tok0 = (long)blockIdx.x * kGateTokens;
     const long arow = tok0 + 16 * tt + r16;                      // this lane's A row (token)
