@@ -13,7 +13,10 @@
 // by load latency.  The d/8 lanes of a head reduce the sum of squares
 // with xor shuffles inside their aligned lane group (fixed order, deterministic).  SiLU and the
 // norm use the hardware reciprocal and reciprocal square root (about 1 ulp each): the division
-// and square root of IEEE fp32 made the kernel issue-bound at 3.7 TB/s.  bf16 rows are read and
+// and square root of IEEE fp32 made the kernel issue-bound at 3.7 TB/s.  The taps are scaled by
+// log2(e) once, so the convolution yields c log2(e) and SiLU's exponential needs no multiply: the
+// factor log2(e) it leaves on silu(c) cancels in the L2 norm (the 1e-12 floor is scaled with it).
+// Heads past H (the last workgroup's spare lanes) compute on head 0's rows and store nothing.  bf16 rows are read and
 // written with non-temporal accesses (each byte is touched once here).
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -91,7 +94,7 @@ prep_kernel(const TIO *__restrict__ x, const float *__restrict__ w, TIO *__restr
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int tau = 0; tau < W; ++tau) wt[j][tau] = w[(long)(c0 + j) * W + tau];
+        for (int tau = 0; tau < W; ++tau) wt[j][tau] = w[(long)(c0 + j) * W + tau] * kLog2e;
 
     // sequence containing t0 and its end
     long seq_start, seq_end;
@@ -139,8 +142,6 @@ prep_kernel(const TIO *__restrict__ x, const float *__restrict__ w, TIO *__restr
             const long t = tb + j;
             float xc[8];
             Vec8<TIO>::unpack(pend[j], xc);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xc[i] = active ? xc[i] : 0.f;  // a select, not a branch
             pend[j] = Vec8<TIO>::load_raw(xc0 + min(t + kPrepPF, t1 - 1) * row);  // token t + kPrepPF
             while (t >= seq_end && (!cu || n + 1 < N)) {  // crossed into the next sequence: zero history
                 if (cu) {
@@ -163,13 +164,13 @@ prep_kernel(const TIO *__restrict__ x, const float *__restrict__ w, TIO *__restr
                 float c = wt[i][W - 1] * xc[i];
 #pragma unroll
                 for (int m = 0; m < W - 1; ++m) c = fmaf(wt[i][m], hist[m][i], c);
-                const float s = c * __builtin_amdgcn_rcpf(1.f + fast_exp2(-c * kLog2e));
+                const float s = c * __builtin_amdgcn_rcpf(1.f + fast_exp2(-c));
                 yv[i] = s;
                 ss = fmaf(s, s, ss);
             }
 #pragma unroll
             for (int off = LPH / 2; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-            const float inv = ss > 1e-24f ? __builtin_amdgcn_rsqf(ss) : 1e12f;  // 1 / max(||y||, 1e-12)
+            const float inv = ss > 1e-24f * kLog2e * kLog2e ? __builtin_amdgcn_rsqf(ss) : 1e12f / kLog2e;
 #pragma unroll
             for (int i = 0; i < 8; ++i) yv[i] *= inv;
             if (active && t < t1) Vec8<TIO>::store(y + t * row + c0, yv);
