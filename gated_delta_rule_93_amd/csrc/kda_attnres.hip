@@ -12,7 +12,8 @@
 //                          softmax (running max, rescaled sum); serves the one-shot read-out and,
 //                          seeded with (o, lse), the phase-2 merge.
 //   attnres_scores_kernel  phase 1a: the scores' dot products w_l . V_n[t] and sum V_n[t]^2 as one
-//                          bf16 MFMA product over the width, rows = 16 tokens of one block.
+//                          bf16 MFMA product over the width, rows = 16 tokens of one block, the
+//                          operands staged in LDS as whole lines.
 //   attnres_mix_kernel     phase 1b: per token, the softmax over the blocks for every layer and the
 //                          weighted sums o_l = sum_n a_ln V_n (the blocks are read once for all L).
 #include <utility>
@@ -127,38 +128,71 @@ __global__ void __launch_bounds__(256) attnres_online_kernel(AttnResArgs a) {
 }
 
 // ---------------------------------------------------------------- phase 1a: score dot products
-// Wave (block b, 16 tokens): rows = tokens, columns = layers (<= 16), k = width in blocks of 32
-// with lane (grp, r16) holding the 8 consecutive width indices 32 kb + 8 grp .. (A and B alike).
-// A second MFMA of the tile with itself gives sum x^2 of each token row on its diagonal.
+// Workgroup (block b, 64 tokens), wave w: rows = the 16 tokens 16 w .., columns = layers (<= 16),
+// k = width in blocks of 32 with lane (grp, r16) holding the 8 consecutive width indices
+// 32 kb + 8 grp .. (A and B alike).  A second MFMA of the tile with itself gives sum x^2 of each
+// token row on its diagonal.  The operands reach the MFMAs through LDS, 256 widths per step: a
+// wave loads its 16 token rows, and the four waves together the 16 query rows (rows past L read
+// row 0 and are zeroed), as whole 128-byte lines (half a wave per 512-byte row segment); loaded
+// directly in the fragment layout every load held 16 rows x 64 bytes and the kernel waited on
+// issuing its loads.  The next step's loads are in flight while the current one is multiplied.
+constexpr int kScoreStep = 256;                  // widths per step
+constexpr int kScoreRow = kScoreStep + 8;        // LDS row (bf16), padded against bank conflicts
 __global__ void __launch_bounds__(256) attnres_scores_kernel(AttnScoreArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[4][16][kScoreRow];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[16][kScoreRow];
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, grp = lane >> 4, r16 = lane & 15;
     const int b = blockIdx.y;
     const long t0 = ((long)blockIdx.x * 4 + wave) * 16;
-    if (t0 >= a.T) return;  // whole wave
-    const long trow = t0 + r16 < a.T ? t0 + r16 : a.T - 1;
-    const uint16_t *xp = a.blk[b] + trow * a.d + 8 * grp;
-    const bool wvalid = r16 < a.L;
-    const uint16_t *wp = a.W + (long)(wvalid ? r16 : 0) * a.d + 8 * grp;
-    const int nkb = a.d / 32;
+    // load j (< 8) of this wave: token row 2 j + (lane >> 5); query load j (< 2): row 4 wave + 2 j +
+    // (lane >> 5); lane & 31 picks the 16-byte piece of the row's 512-byte step.  Rows past the
+    // end are read from a valid row (tokens: the last one; queries: row 0, then zeroed).
+    const int half = lane >> 5, piece = 8 * (lane & 31);
+    const uint16_t *xl[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const long t = t0 + 2 * j + half;
+        xl[j] = a.blk[b] + (t < a.T ? t : a.T - 1) * a.d + piece;
+    }
+    const uint16_t *wl[2];
+    bool wok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 4 * wave + 2 * j + half;
+        wok[j] = row < a.L;
+        wl[j] = a.W + (long)(wok[j] ? row : 0) * a.d + piece;
+    }
+    const int nsteps = a.d / kScoreStep;
+    auto issue = [&](int st, u32x4 (&xr)[8], u32x4 (&wr)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xr[j] = *reinterpret_cast<const u32x4 *>(xl[j] + (long)kScoreStep * st);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) wr[j] = *reinterpret_cast<const u32x4 *>(wl[j] + (long)kScoreStep * st);
+    };
     f32x4 dots = zero4(), sq = zero4();
-    for (int kb = 0; kb < nkb; kb += 8) {  // d is a multiple of 512: whole steps of eight
-        u32x4 xv[8], wv[8];
+    // one step: the registers to LDS, the next step's loads issued, then the 16 MFMAs from LDS
+    auto step = [&](int st, u32x4 (&xr)[8], u32x4 (&wr)[2], u32x4 (&xn)[8], u32x4 (&wn)[2]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            xv[i] = *reinterpret_cast<const u32x4 *>(xp + 32 * (kb + i));
-            wv[i] = *reinterpret_cast<const u32x4 *>(wp + 32 * (kb + i));
-        }
-        // all sixteen loads in flight before the MFMAs that use them
-        asm volatile("" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]), "+v"(xv[4]), "+v"(xv[5]),
-                          "+v"(xv[6]), "+v"(xv[7]), "+v"(wv[0]), "+v"(wv[1]), "+v"(wv[2]), "+v"(wv[3]),
-                          "+v"(wv[4]), "+v"(wv[5]), "+v"(wv[6]), "+v"(wv[7]));
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(&xs[wave][2 * j + half][piece]) = xr[j];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const FragB xa{__builtin_bit_cast(bf16x8, xv[i])};
-            const FragB wb{__builtin_bit_cast(bf16x8, wvalid ? wv[i] : u32x4{0u, 0u, 0u, 0u})};
+        for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<u32x4 *>(&ws[4 * wave + 2 * j + half][piece]) = wok[j] ? wr[j] : u32x4{0u, 0u, 0u, 0u};
+        if (st + 1 < nsteps) issue(st + 1, xn, wn);
+        __syncthreads();  // the step's query rows (written by all four waves) are in LDS
+#pragma unroll
+        for (int kb = 0; kb < kScoreStep / 32; ++kb) {
+            const FragB xa{__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&xs[wave][r16][32 * kb + 8 * grp]))};
+            const FragB wb{__builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(&ws[r16][32 * kb + 8 * grp]))};
             dots = mfma(xa, wb, dots);
             sq = mfma(xa, xa, sq);
         }
+        __syncthreads();  // every wave is done with the step's rows before they are overwritten
+    };
+    u32x4 xA[8], wA[2], xB[8], wB[2];
+    issue(0, xA, wA);
+    for (int st = 0; st < nsteps; st += 2) {  // nsteps is even (d is a multiple of 512)
+        step(st, xA, wA, xB, wB);
+        step(st + 1, xB, wB, xA, wA);
     }
     // lane (grp, r16) holds rows 4 grp + e, column r16
 #pragma unroll
