@@ -163,10 +163,9 @@ __device__ __forceinline__ int kslot(int grp, int s) { return 16 * (s >> 2) + 4 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Index of the calling wave in its one-dimensional workgroup, as a scalar (wave-uniform) value, so
-// that branches on it compile to scalar branches, not to EXEC-masked regions: a matrix instruction
-// inside an EXEC-masked region whose result is used after the region gave wrong results (a copy of
-// the state scan with two column tiles per wave produced wrong output rows with the branch, correct
-// ones without it).
+// that branches on it compile to scalar branches, not to EXEC-masked regions.  An MFMA under an
+// EXEC-masked branch whose result is used after the branch was observed to give wrong results;
+// with a scalar condition no such region is formed.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 }  // namespace kda

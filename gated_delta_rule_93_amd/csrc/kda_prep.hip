@@ -16,8 +16,8 @@
 // and square root of IEEE fp32 made the kernel issue-bound at 3.7 TB/s.  The taps are scaled by
 // log2(e) once, so the convolution yields c log2(e) and SiLU's exponential needs no multiply: the
 // factor log2(e) it leaves on silu(c) cancels in the L2 norm (the 1e-12 floor is scaled with it).
-// Heads past H (the last workgroup's spare lanes) compute on head 0's rows and store nothing.  bf16 rows are read and
-// written with non-temporal accesses (each byte is touched once here).
+// Heads past H (the last workgroup's spare lanes) compute on head 0's rows and store nothing.
+// bf16 rows are read and written with non-temporal accesses (each byte is touched once here).
 #include "kda_common.h"
 #include "kda_internal.h"
 
